@@ -1,0 +1,287 @@
+"""ctypes binding of libskv (include/skv.h): argument marshalling only.
+
+Every function here takes torch tensors, checks that they are contiguous device tensors of
+the right dtype, derives the sizes the C call needs, and calls the C entry point of the same
+name on torch's current HIP stream. All arithmetic runs in the library's HIP kernels; there
+is no fallback of any kind: if libskv.so is missing this module fails to import.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libskv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m streaming_kv_cache_write_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+
+# ------------------------------------------------------------------------------ constants
+SKV_OK, SKV_ERR_NULL, SKV_ERR_SHAPE, SKV_ERR_RANGE, SKV_ERR_DTYPE, SKV_ERR_ALIGN, \
+    SKV_ERR_UNSUPPORTED, SKV_ERR_HIP = range(8)
+STATUS_NAMES = ["SKV_OK", "SKV_ERR_NULL", "SKV_ERR_SHAPE", "SKV_ERR_RANGE", "SKV_ERR_DTYPE",
+                "SKV_ERR_ALIGN", "SKV_ERR_UNSUPPORTED", "SKV_ERR_HIP"]
+SKV_F32, SKV_F16, SKV_BF16 = 0, 1, 2
+MASK_NONE, MASK_CAUSAL, MASK_BLOCK_CAUSAL = 0, 1, 2
+FULL_CAPACITY_MASKED = 1
+DEV_INDEX_RANGE, DEV_KV_LEN, DEV_CU_SEQLENS, DEV_RING_UNRESERVED, DEV_CURSOR_FULL = 1, 2, 4, 8, 16
+
+_DTYPES = {torch.float32: SKV_F32, torch.float16: SKV_F16, torch.bfloat16: SKV_BF16}
+
+
+class SkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{name}: {message}")
+
+
+class skv_attn_params(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("Tq", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int),
+        ("D", ctypes.c_int),
+        ("dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+        ("cap", ctypes.c_int), ("kv_len", ctypes.c_int),
+        ("kv_len_dev", ctypes.c_void_p), ("cu_seqlens_kv_dev", ctypes.c_void_p),
+        ("max_seqlen_kv", ctypes.c_int),
+        ("mask", ctypes.c_int), ("mask_block", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("flags", ctypes.c_uint),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("err_dev", ctypes.c_void_p),
+    ]
+
+
+_vp, _i, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "skv_last_error": (ctypes.c_char_p, []),
+    "skv_version": (ctypes.c_char_p, []),
+    "kv_write_indexed": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "kv_cursor_advance": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "kv_ring_meta_bytes": (_sz, [_i]),
+    "kv_ring_create": (_i, [ctypes.POINTER(_vp), _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "kv_ring_reserve": (_i, [_vp, _vp, _vp]),
+    "kv_ring_write": (_i, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "kv_ring_reset": (_i, [_vp, _vp, _vp]),
+    "kv_ring_kv_len_dev": (_vp, [_vp]),
+    "kv_ring_slot_dev": (_vp, [_vp]),
+    "kv_ring_destroy": (_i, [_vp]),
+    "attn_workspace_bytes": (_sz, [ctypes.POINTER(skv_attn_params)]),
+    "attn_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, ctypes.POINTER(skv_attn_params), _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+EXPORTED = tuple(_SIGS)
+
+
+def _check(status: int) -> None:
+    if status != SKV_OK:
+        raise SkvError(status, lib.skv_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev_tensor(t, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _DTYPES[dtype]
+
+
+# ------------------------------------------------------------------------------ writes
+def kv_write_indexed(k_cache, v_cache, k_src, v_src, index=None, start: int = 0, err=None):
+    """k_cache[b, index[t]] = k_src[b, t] (and V); index None -> rows start .. start+n."""
+    _dev_tensor(k_cache, "k_cache")
+    B, cap, Hkv, D = k_cache.shape
+    _dev_tensor(k_src, "k_src", k_cache.dtype)
+    if v_cache is not None:
+        _dev_tensor(v_cache, "v_cache", k_cache.dtype)
+        _dev_tensor(v_src, "v_src", k_cache.dtype)
+    if index is not None:
+        _dev_tensor(index, "index", torch.int64)
+    if err is not None:
+        _dev_tensor(err, "err", torch.int32)
+    n = k_src.shape[1]
+    _check(lib.kv_write_indexed(_ptr(k_cache), _ptr(v_cache), _ptr(k_src), _ptr(v_src), _ptr(index),
+                                int(start), B, cap, n, Hkv, D, dtype_code(k_cache.dtype), _ptr(err),
+                                _stream(k_cache.device)))
+
+
+def kv_cursor_advance(cursor, n: int, cap: int, index_out, kv_len_out=None, err=None):
+    """index_out[t] = cursor + t, kv_len_out[:] = cursor + n, cursor += n, all on the device."""
+    _dev_tensor(cursor, "cursor", torch.int32)
+    _dev_tensor(index_out, "index_out", torch.int64)
+    B = 0
+    if kv_len_out is not None:
+        _dev_tensor(kv_len_out, "kv_len_out", torch.int32)
+        B = kv_len_out.numel()
+    if err is not None:
+        _dev_tensor(err, "err", torch.int32)
+    _check(lib.kv_cursor_advance(_ptr(cursor), int(n), int(cap), B, _ptr(index_out),
+                                 _ptr(kv_len_out), _ptr(err), _stream(cursor.device)))
+
+
+class Ring:
+    """Sink-plus-window ring over caller storage k_store/v_store [B, n_slots*chunk, Hkv, D]."""
+
+    def __init__(self, k_store, v_store, chunk: int, n_slots: int, sink_slots: int, meta=None):
+        _dev_tensor(k_store, "k_store")
+        B, rows, Hkv, D = k_store.shape
+        if rows != n_slots * chunk:
+            raise ValueError(f"storage has {rows} rows, expected n_slots*chunk = {n_slots * chunk}")
+        if v_store is not None:
+            _dev_tensor(v_store, "v_store", k_store.dtype)
+        nbytes = lib.kv_ring_meta_bytes(B)
+        if meta is None:
+            meta = torch.empty(nbytes // 4, dtype=torch.int32, device=k_store.device)
+        _dev_tensor(meta, "meta", torch.int32)
+        if meta.numel() * 4 < nbytes:
+            raise ValueError("meta buffer too small")
+        self.k_store, self.v_store, self.meta = k_store, v_store, meta
+        self.B, self.chunk, self.n_slots, self.sink = B, chunk, n_slots, sink_slots
+        self._h = ctypes.c_void_p()
+        _check(lib.kv_ring_create(ctypes.byref(self._h), _ptr(k_store), _ptr(v_store), _ptr(meta),
+                                  B, chunk, n_slots, sink_slots, Hkv, D, dtype_code(k_store.dtype),
+                                  _stream(k_store.device)))
+
+    @property
+    def handle(self) -> int:
+        return self._h.value
+
+    def reserve(self, batch_mask=None):
+        if batch_mask is not None:
+            _dev_tensor(batch_mask, "batch_mask", torch.uint8)
+        _check(lib.kv_ring_reserve(self._h, _ptr(batch_mask), _stream(self.k_store.device)))
+
+    def write(self, k_src, v_src=None, batch_mask=None, err=None):
+        _dev_tensor(k_src, "k_src", self.k_store.dtype)
+        if v_src is not None:
+            _dev_tensor(v_src, "v_src", self.k_store.dtype)
+        if batch_mask is not None:
+            _dev_tensor(batch_mask, "batch_mask", torch.uint8)
+        if err is not None:
+            _dev_tensor(err, "err", torch.int32)
+        if k_src.shape[0] != self.B or k_src.shape[1] != self.chunk:
+            raise ValueError(f"source must be [B={self.B}, chunk={self.chunk}, Hkv, D]")
+        _check(lib.kv_ring_write(self._h, _ptr(k_src), _ptr(v_src), _ptr(batch_mask), _ptr(err),
+                                 _stream(self.k_store.device)))
+
+    def reset(self, batch_mask=None):
+        if batch_mask is not None:
+            _dev_tensor(batch_mask, "batch_mask", torch.uint8)
+        _check(lib.kv_ring_reset(self._h, _ptr(batch_mask), _stream(self.k_store.device)))
+
+    @property
+    def kv_len(self):
+        """[B] int32 device view of the retained-token counts (attention's kv_len_dev)."""
+        return self.meta[3 * self.B:4 * self.B]
+
+    @property
+    def slot(self):
+        return self.meta[self.B:2 * self.B]
+
+    @property
+    def counter(self):
+        return self.meta[:self.B]
+
+    def close(self):
+        if self._h:
+            lib.kv_ring_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------------------ attention
+def make_params(q, k, *, kv_len=None, kv_len_dev=None, cu_seqlens_kv=None, max_seqlen_kv=0,
+                mask=MASK_NONE, mask_block=1, scale=0.0, full_capacity_masked=False,
+                out_dtype=None, workspace=None, err=None) -> skv_attn_params:
+    B, Tq, Hq, D = q.shape
+    if cu_seqlens_kv is not None:
+        cap, Hkv = k.shape[0], k.shape[1]
+    else:
+        if k.shape[0] != B:
+            raise ValueError(f"k has batch {k.shape[0]}, q has {B}")
+        cap, Hkv = k.shape[1], k.shape[2]
+    p = skv_attn_params()
+    p.B, p.Tq, p.Hq, p.Hkv, p.D = B, Tq, Hq, Hkv, D
+    p.dtype = dtype_code(q.dtype)
+    p.out_dtype = dtype_code(out_dtype) if out_dtype is not None else p.dtype
+    p.cap = cap
+    p.kv_len = int(kv_len) if kv_len is not None else 0
+    p.kv_len_dev = _ptr(kv_len_dev)
+    p.cu_seqlens_kv_dev = _ptr(cu_seqlens_kv)
+    p.max_seqlen_kv = int(max_seqlen_kv)
+    p.mask, p.mask_block = int(mask), int(mask_block)
+    p.scale = float(scale)
+    p.flags = FULL_CAPACITY_MASKED if full_capacity_masked else 0
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    p.err_dev = _ptr(err)
+    return p
+
+
+def attn_workspace_bytes(q, k, **kw) -> int:
+    return int(lib.attn_workspace_bytes(ctypes.byref(make_params(q, k, **kw))))
+
+
+def attn_chunk_fwd(q, k, v, out=None, lse=None, *, kv_len=None, kv_len_dev=None,
+                   cu_seqlens_kv=None, max_seqlen_kv=0, mask=MASK_NONE, mask_block=1, scale=0.0,
+                   full_capacity_masked=False, out_dtype=None, workspace=None, err=None):
+    """Attention of q [B, Tq, Hq, D] over k/v [B, cap, Hkv, D] (prefix: host kv_len or device
+    kv_len_dev [B] int32) or packed k/v [total, Hkv, D] (cu_seqlens_kv [B+1] int32).
+    Returns out [B, Tq, Hq, D] (and fills lse [B, Hq, Tq] fp32 if given)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(k, "k", q.dtype)
+    _dev_tensor(v, "v", q.dtype)
+    if kv_len_dev is not None:
+        _dev_tensor(kv_len_dev, "kv_len_dev", torch.int32)
+    if cu_seqlens_kv is not None:
+        _dev_tensor(cu_seqlens_kv, "cu_seqlens_kv", torch.int32)
+    if err is not None:
+        _dev_tensor(err, "err", torch.int32)
+    odt = out_dtype if out_dtype is not None else q.dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    _dev_tensor(out, "out", odt)
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32)
+    kw = dict(kv_len=kv_len, kv_len_dev=kv_len_dev, cu_seqlens_kv=cu_seqlens_kv,
+              max_seqlen_kv=max_seqlen_kv, mask=mask, mask_block=mask_block, scale=scale,
+              full_capacity_masked=full_capacity_masked, out_dtype=odt, err=err)
+    if workspace is None:
+        need = attn_workspace_bytes(q, k, **kw)
+        if need:  # zero-filled: the split-K arrival counters must start at zero
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace")
+    p = make_params(q, k, workspace=workspace, **kw)
+    _check(lib.attn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), ctypes.byref(p),
+                              _stream(q.device)))
+    return out

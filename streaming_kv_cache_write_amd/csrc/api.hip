@@ -1,0 +1,288 @@
+// Host side of the libskv C ABI: argument validation, dispatch, launches on the caller's
+// stream. Nothing here allocates device memory, synchronizes, or reads device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <string>
+
+#include "common.h"
+
+namespace skv {
+hipError_t launch_write_indexed(const void*, const void*, void*, void*, const int64_t*, int64_t, int,
+                                int, int, int, int32_t*, hipStream_t);
+hipError_t launch_cursor_advance(int32_t*, int, int, int, int64_t*, int32_t*, int32_t*, hipStream_t);
+hipError_t launch_ring_reset(int32_t*, int, const uint8_t*, hipStream_t);
+hipError_t launch_ring_reserve(int32_t*, int, const uint8_t*, int, int, hipStream_t);
+hipError_t launch_ring_write(const void*, const void*, void*, void*, int32_t*, int, const uint8_t*,
+                             int, int, int, int32_t*, hipStream_t);
+hipError_t launch_attn_f32(const AttnArgs&, int, hipStream_t);
+hipError_t launch_attn_flash(const AttnArgs&, int, int, int, hipStream_t);
+hipError_t launch_attn_decode(const AttnArgs&, int, int, int, void*, int, hipStream_t);
+int decode_splits(int B, int Hkv, int max_len);
+size_t decode_workspace_bytes(int B, int Hkv, int D, int n_splits);
+}  // namespace skv
+
+using namespace skv;
+
+namespace {
+
+thread_local std::string g_err;
+
+skv_status fail(skv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+skv_status ok() {
+  g_err.clear();
+  return SKV_OK;
+}
+
+skv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(int dtype) {
+  switch (dtype) {
+    case SKV_F32: return 4;
+    case SKV_F16: return 2;
+    case SKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kDecodeMaxTq = 4;
+constexpr int kDecodeMaxRows = 16;
+
+// Path taken by attn_chunk_fwd for a validated parameter set.
+enum Path { PATH_F32, PATH_FLASH, PATH_DECODE };
+
+Path choose_path(const skv_attn_params& p) {
+  if (p.dtype == SKV_F32) return PATH_F32;
+  if (p.Tq <= kDecodeMaxTq && p.Tq * (p.Hq / p.Hkv) <= kDecodeMaxRows) return PATH_DECODE;
+  return PATH_FLASH;
+}
+
+int decode_max_len(const skv_attn_params& p) {
+  if (p.flags & SKV_FULL_CAPACITY_MASKED) return p.cap;
+  if (p.cu_seqlens_kv_dev || p.kv_len_dev)
+    return p.max_seqlen_kv > 0 ? (p.max_seqlen_kv < p.cap ? p.max_seqlen_kv : p.cap) : p.cap;
+  return p.kv_len;
+}
+
+skv_status validate_attn(const void* q, const void* k, const void* v, const void* out,
+                         const skv_attn_params* p) {
+  if (!p) return fail(SKV_ERR_NULL, "params is NULL");
+  if (!q || !k || !v || !out) return fail(SKV_ERR_NULL, "q, k, v and out must be non-NULL");
+  const bool packed = p->cu_seqlens_kv_dev != nullptr;
+  if (packed && p->kv_len_dev)
+    return fail(SKV_ERR_UNSUPPORTED, "kv_len_dev and cu_seqlens_kv_dev are exclusive");
+  if (packed && (p->flags & SKV_FULL_CAPACITY_MASKED))
+    return fail(SKV_ERR_UNSUPPORTED, "the full-capacity arm needs prefix (slab) mode");
+  if (p->B < 1 || p->Tq < 0 || p->Hq < 1 || p->Hkv < 1)
+    return fail(SKV_ERR_SHAPE, "need B >= 1, Tq >= 0, Hq >= 1, Hkv >= 1 (got %d, %d, %d, %d)",
+                p->B, p->Tq, p->Hq, p->Hkv);
+  if (p->Hq % p->Hkv) return fail(SKV_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
+  if (p->D != 64 && p->D != 128) return fail(SKV_ERR_UNSUPPORTED, "head dim D=%d (supported: 64, 128)", p->D);
+  if (!elem_bytes(p->dtype)) return fail(SKV_ERR_DTYPE, "unknown dtype %d", p->dtype);
+  if (p->out_dtype != p->dtype && p->out_dtype != SKV_F32)
+    return fail(SKV_ERR_DTYPE, "out_dtype must equal dtype or be SKV_F32");
+  if (p->cap < 1) return fail(SKV_ERR_SHAPE, "cap must be >= 1 (got %d)", p->cap);
+  if (p->mask < SKV_MASK_NONE || p->mask > SKV_MASK_BLOCK_CAUSAL)
+    return fail(SKV_ERR_RANGE, "unknown mask %d", p->mask);
+  if (p->mask == SKV_MASK_BLOCK_CAUSAL && p->mask_block < 1)
+    return fail(SKV_ERR_RANGE, "mask_block must be >= 1 (got %d)", p->mask_block);
+  if (p->flags & ~(unsigned)SKV_FULL_CAPACITY_MASKED) return fail(SKV_ERR_RANGE, "unknown flags 0x%x", p->flags);
+  if (!(p->scale >= 0.f) || isinf(p->scale)) return fail(SKV_ERR_RANGE, "scale must be finite and >= 0");
+  if (!packed && !p->kv_len_dev) {
+    if (p->kv_len < 1 || p->kv_len > p->cap)
+      return fail(SKV_ERR_RANGE, "kv_len=%d outside [1, cap=%d]", p->kv_len, p->cap);
+    if (p->mask != SKV_MASK_NONE && p->Tq > p->kv_len)
+      return fail(SKV_ERR_RANGE, "masked chunk of Tq=%d queries longer than kv_len=%d", p->Tq, p->kv_len);
+  }
+  if (p->max_seqlen_kv < 0) return fail(SKV_ERR_RANGE, "max_seqlen_kv must be >= 0");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(SKV_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
+  const int64_t elems = (int64_t)p->B * p->Tq * p->Hq;
+  if (elems > 0x7fffffff) return fail(SKV_ERR_SHAPE, "B*Tq*Hq too large");
+  return SKV_OK;
+}
+
+}  // namespace
+
+struct skv_ring {
+  void* k_store;
+  void* v_store;
+  int32_t* meta;
+  int B, chunk, n_slots, sink, Hkv, D, dtype;
+  int vpr;  // 16-byte vectors per cache row
+};
+
+extern "C" {
+
+const char* skv_last_error(void) { return g_err.c_str(); }
+const char* skv_version(void) { return "libskv 0.1 (gfx950)"; }
+
+skv_status kv_write_indexed(void* k_cache, void* v_cache, const void* k_src, const void* v_src,
+                            const int64_t* index_dev, int64_t start, int B, int cap, int n,
+                            int Hkv, int D, int dtype, int32_t* err_dev, void* stream) {
+  if (!k_cache || !k_src) return fail(SKV_ERR_NULL, "k_cache and k_src must be non-NULL");
+  if ((v_cache == nullptr) != (v_src == nullptr))
+    return fail(SKV_ERR_NULL, "v_cache and v_src must both be given or both be NULL");
+  if (!elem_bytes(dtype)) return fail(SKV_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (B < 0 || n < 0 || cap < 1 || Hkv < 1 || D < 1)
+    return fail(SKV_ERR_SHAPE, "bad sizes B=%d cap=%d n=%d Hkv=%d D=%d", B, cap, n, Hkv, D);
+  const int64_t row_bytes = (int64_t)Hkv * D * elem_bytes(dtype);
+  if (row_bytes % 16) return fail(SKV_ERR_ALIGN, "row of Hkv*D elements (%lld bytes) is not a multiple of 16", (long long)row_bytes);
+  if (!aligned16(k_cache) || !aligned16(k_src) || !aligned16(v_cache) || !aligned16(v_src))
+    return fail(SKV_ERR_ALIGN, "cache and source pointers must be 16-byte aligned");
+  if (!index_dev && (start < 0 || start + n > cap))
+    return fail(SKV_ERR_RANGE, "rows [%lld, %lld) outside the cache of %d rows", (long long)start,
+                (long long)(start + n), cap);
+  if ((int64_t)B * n > 0x7fffffff) return fail(SKV_ERR_SHAPE, "B*n too large");
+  if (B == 0 || n == 0) return ok();
+  return hip_status(launch_write_indexed(k_src, v_src, k_cache, v_cache, index_dev, start, B, n,
+                                         cap, (int)(row_bytes / 16), err_dev, (hipStream_t)stream),
+                    "kv_write_indexed launch");
+}
+
+skv_status kv_cursor_advance(int32_t* cursor_dev, int n, int cap, int B, int64_t* index_out_dev,
+                             int32_t* kv_len_out_dev, int32_t* err_dev, void* stream) {
+  if (!cursor_dev || !index_out_dev) return fail(SKV_ERR_NULL, "cursor_dev and index_out_dev must be non-NULL");
+  if (n < 1 || cap < 1 || B < 0) return fail(SKV_ERR_SHAPE, "need n >= 1, cap >= 1, B >= 0");
+  if (((uintptr_t)cursor_dev & 3) || ((uintptr_t)index_out_dev & 7) || ((uintptr_t)kv_len_out_dev & 3))
+    return fail(SKV_ERR_ALIGN, "misaligned cursor / index / kv_len pointer");
+  return hip_status(launch_cursor_advance(cursor_dev, n, cap, B, index_out_dev, kv_len_out_dev,
+                                          err_dev, (hipStream_t)stream),
+                    "kv_cursor_advance launch");
+}
+
+size_t kv_ring_meta_bytes(int B) { return B > 0 ? (size_t)B * 4 * sizeof(int32_t) : 0; }
+
+skv_status kv_ring_create(skv_ring** out, void* k_store, void* v_store, void* meta_dev, int B,
+                          int chunk, int n_slots, int sink_slots, int Hkv, int D, int dtype,
+                          void* stream) {
+  if (!out || !k_store || !meta_dev) return fail(SKV_ERR_NULL, "out, k_store and meta_dev must be non-NULL");
+  *out = nullptr;
+  if (!elem_bytes(dtype)) return fail(SKV_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (B < 1 || chunk < 1 || Hkv < 1 || D < 1) return fail(SKV_ERR_SHAPE, "bad ring sizes");
+  if (n_slots < 1 || sink_slots < 0 || sink_slots >= n_slots)
+    return fail(SKV_ERR_RANGE, "need 0 <= sink_slots (%d) < n_slots (%d)", sink_slots, n_slots);
+  if ((int64_t)n_slots * chunk > 0x7fffffff || (int64_t)B * chunk > 0x7fffffff)
+    return fail(SKV_ERR_SHAPE, "ring too large");
+  const int64_t row_bytes = (int64_t)Hkv * D * elem_bytes(dtype);
+  if (row_bytes % 16) return fail(SKV_ERR_ALIGN, "row bytes not a multiple of 16");
+  if (!aligned16(k_store) || !aligned16(v_store) || ((uintptr_t)meta_dev & 3))
+    return fail(SKV_ERR_ALIGN, "misaligned ring storage or metadata");
+  skv_ring* r = (skv_ring*)malloc(sizeof(skv_ring));
+  if (!r) return fail(SKV_ERR_RANGE, "out of host memory");
+  *r = skv_ring{k_store, v_store, (int32_t*)meta_dev, B, chunk, n_slots, sink_slots, Hkv, D, dtype,
+                (int)(row_bytes / 16)};
+  hipError_t e = launch_ring_reset(r->meta, B, nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    free(r);
+    return hip_status(e, "kv_ring_create launch");
+  }
+  *out = r;
+  return ok();
+}
+
+skv_status kv_ring_reserve(skv_ring* r, const uint8_t* batch_mask_dev, void* stream) {
+  if (!r) return fail(SKV_ERR_NULL, "ring is NULL");
+  return hip_status(launch_ring_reserve(r->meta, r->B, batch_mask_dev, r->n_slots, r->sink,
+                                        (hipStream_t)stream),
+                    "kv_ring_reserve launch");
+}
+
+skv_status kv_ring_write(skv_ring* r, const void* k_src, const void* v_src,
+                         const uint8_t* batch_mask_dev, int32_t* err_dev, void* stream) {
+  if (!r) return fail(SKV_ERR_NULL, "ring is NULL");
+  if (!k_src) return fail(SKV_ERR_NULL, "k_src is NULL");
+  if ((r->v_store == nullptr) != (v_src == nullptr))
+    return fail(SKV_ERR_NULL, "v_src must be given iff the ring has V storage");
+  if (!aligned16(k_src) || !aligned16(v_src)) return fail(SKV_ERR_ALIGN, "sources must be 16-byte aligned");
+  return hip_status(launch_ring_write(k_src, v_src, r->k_store, r->v_store, r->meta, r->B,
+                                      batch_mask_dev, r->chunk, r->n_slots, r->vpr, err_dev,
+                                      (hipStream_t)stream),
+                    "kv_ring_write launch");
+}
+
+skv_status kv_ring_reset(skv_ring* r, const uint8_t* batch_mask_dev, void* stream) {
+  if (!r) return fail(SKV_ERR_NULL, "ring is NULL");
+  return hip_status(launch_ring_reset(r->meta, r->B, batch_mask_dev, (hipStream_t)stream),
+                    "kv_ring_reset launch");
+}
+
+const int32_t* kv_ring_kv_len_dev(const skv_ring* r) { return r ? r->meta + 3 * r->B : nullptr; }
+const int32_t* kv_ring_slot_dev(const skv_ring* r) { return r ? r->meta + r->B : nullptr; }
+
+skv_status kv_ring_destroy(skv_ring* r) {
+  free(r);
+  return ok();
+}
+
+size_t attn_workspace_bytes(const skv_attn_params* p) {
+  if (!p || validate_attn((void*)16, (void*)16, (void*)16, (void*)16, p) != SKV_OK) return 0;
+  if (choose_path(*p) != PATH_DECODE) return 0;
+  const int splits = decode_splits(p->B, p->Hkv, decode_max_len(*p));
+  return decode_workspace_bytes(p->B, p->Hkv, p->D, splits);
+}
+
+skv_status attn_chunk_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const skv_attn_params* p, void* stream) {
+  skv_status st = validate_attn(q, k, v, out, p);
+  if (st != SKV_OK) return st;
+  if (lse && ((uintptr_t)lse & 3)) return fail(SKV_ERR_ALIGN, "lse must be 4-byte aligned");
+  if (p->Tq == 0) return ok();
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.kv_len_dev = p->kv_len_dev;
+  a.cu = p->cu_seqlens_kv_dev;
+  a.err = p->err_dev;
+  a.B = p->B;
+  a.Tq = p->Tq;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.cap = p->cap;
+  a.kv_len_host = p->kv_len;
+  a.mask = p->mask;
+  a.block = p->mask == SKV_MASK_BLOCK_CAUSAL ? p->mask_block : 1;
+  a.full_cap = (p->flags & SKV_FULL_CAPACITY_MASKED) ? 1 : 0;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+  switch (choose_path(*p)) {
+    case PATH_F32:
+      return hip_status(launch_attn_f32(a, p->D, s), "attn_chunk_fwd (fp32) launch");
+    case PATH_FLASH:
+      return hip_status(launch_attn_flash(a, p->dtype, p->out_dtype, p->D, s),
+                        "attn_chunk_fwd (flash) launch");
+    case PATH_DECODE: {
+      const int splits = decode_splits(p->B, p->Hkv, decode_max_len(*p));
+      const size_t need = decode_workspace_bytes(p->B, p->Hkv, p->D, splits);
+      if (!p->workspace) return fail(SKV_ERR_NULL, "decode-sized call needs a workspace of %zu bytes", need);
+      if (p->workspace_bytes < need)
+        return fail(SKV_ERR_RANGE, "workspace of %zu bytes < %zu required", p->workspace_bytes, need);
+      if (!aligned16(p->workspace)) return fail(SKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+      return hip_status(launch_attn_decode(a, p->dtype, p->out_dtype, p->D, p->workspace, splits, s),
+                        "attn_chunk_fwd (decode) launch");
+    }
+  }
+  return fail(SKV_ERR_UNSUPPORTED, "no path");
+}
+
+}  // extern "C"
