@@ -1,0 +1,477 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-cache write + chunk-attention hot path on one MI355X.
+
+Headline workload (one "step" = one whole job): autoregressive decode with an active prefix,
+B=1, 32 query heads on 8 KV heads, D=128, bf16, cache capacity 32768 rows: a 234-token causal
+prefill (cursor advance, indexed write of 234 rows, flash attention) followed by 1024 decode
+steps, each a cursor advance, a one-row indexed write and a split-K attention over the
+active prefix kv_len = 235 ... 1258. The job is recorded once into a HIP graph and replayed;
+all inputs are resident in HBM before the timed region starts.
+
+Printed as one JSON line:
+  value         decode KV-read throughput of the whole job: the K/V bytes the job's attention
+                calls must read (active prefix only) / job time, in GB/s;
+  roofline      the dominant kernel (split-K decode attention): algorithmic bytes per launch
+                (K/V prefix + Q + O) / its mean duration, measured with HIP events around each
+                launch on the launch stream, against 8 TB/s HBM;
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same job;
+  rows          the other hot-path workloads measured in the same run (ring, multi-user slab,
+                ragged cross-attention, decode kv_len sweep with cold caches, slab writes).
+
+`python bench.py --gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2516.6    # MI355X dense bf16 matrix peak, published (256 CU x 2.4 GHz x 4096)
+ELEM = 2                       # bytes per bf16/fp16 element
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--only", default="", help="profiling aid: run only this part "
+                    "(decode | ring | multiuser | ragged | sweep | write)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------------------
+# timing helpers
+# ----------------------------------------------------------------------------------------
+def event_pair(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_gpu(torch, fn, reps=10, warm=2, flush=None):
+    """Median GPU time (ms) of fn() measured with events on the current stream. If flush is
+    given it runs (untimed) before every repetition to evict L2 and the Infinity Cache."""
+    for _ in range(warm):
+        fn()
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = event_pair(torch)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return statistics.median(times)
+
+
+def make_flush(torch, dev):
+    """Overwrite a 1 GiB buffer: larger than 2 x (32 MB L2 + 256 MB Infinity Cache)."""
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    return lambda: buf.fill_(1)
+
+
+# ----------------------------------------------------------------------------------------
+# headline: decode job
+# ----------------------------------------------------------------------------------------
+class DecodeJob:
+    """Prefill + 1024 decode steps through the device cursor; everything device-resident."""
+
+    def __init__(self, torch, skv, SI, dev, dtype):
+        W = SI.Decode()
+        self.W, self.torch, self.skv = W, torch, skv
+        n = W.prompt + W.steps
+        td = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+        self.q = SI.per_batch_device_normal(1, (n, W.Hq, W.D), "decode", "q", dev, dtype, std=W.std)
+        self.k = SI.per_batch_device_normal(1, (n, W.Hkv, W.D), "decode", "k", dev, dtype, std=W.std)
+        self.v = SI.per_batch_device_normal(1, (n, W.Hkv, W.D), "decode", "v", dev, dtype, std=W.std)
+        self.kc = torch.zeros(1, W.cap, W.Hkv, W.D, dtype=td, device=dev)
+        self.vc = torch.zeros_like(self.kc)
+        self.cursor = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.kv_len = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.idx_pre = torch.empty(W.prompt, dtype=torch.int64, device=dev)
+        self.idx_one = torch.empty(1, dtype=torch.int64, device=dev)
+        self.out_pre = torch.empty(1, W.prompt, W.Hq, W.D, dtype=td, device=dev)
+        self.out = torch.empty(W.steps, 1, 1, W.Hq, W.D, dtype=td, device=dev)
+        T = W.prompt
+        # the job's longest prefix bounds the split-K grid (device kv_len, fixed launch shape)
+        self.max_kv = T + W.steps
+        self.ws = torch.zeros(skv.attn_workspace_bytes(self.q[:, T:T + 1], self.kc, kv_len_dev=self.kv_len,
+                                                       max_seqlen_kv=self.max_kv), dtype=torch.uint8,
+                              device=dev)
+        # prebuilt views so the replayed sequence does no tensor bookkeeping
+        self.q_pre, self.k_pre, self.v_pre = self.q[:, :T], self.k[:, :T], self.v[:, :T]
+        self.q_steps = [self.q[:, T + i:T + i + 1] for i in range(W.steps)]
+        self.k_steps = [self.k[:, T + i:T + i + 1] for i in range(W.steps)]
+        self.v_steps = [self.v[:, T + i:T + i + 1] for i in range(W.steps)]
+        # algorithmic bytes: K/V of the active prefix (+ Q and O for the per-launch figure)
+        self.kv_bytes_job = sum(2 * (T + i + 1) * W.Hkv * W.D * ELEM for i in range(W.steps)) \
+            + 2 * T * W.Hkv * W.D * ELEM
+        self.decode_launch_bytes = [2 * (T + i + 1) * W.Hkv * W.D * ELEM + 2 * W.Hq * W.D * ELEM
+                                    for i in range(W.steps)]
+
+    def run(self, events=None):
+        skv, W = self.skv, self.W
+        self.cursor.zero_()  # a fill kernel, not a memset: safe to record in a graph
+        skv.kv_cursor_advance(self.cursor, W.prompt, W.cap, self.idx_pre, self.kv_len)
+        skv.kv_write_indexed(self.kc, self.vc, self.k_pre, self.v_pre, index=self.idx_pre)
+        skv.attn_chunk_fwd(self.q_pre, self.kc, self.vc, self.out_pre, kv_len_dev=self.kv_len,
+                           mask=skv.MASK_CAUSAL, max_seqlen_kv=W.cap)
+        for i in range(W.steps):
+            skv.kv_cursor_advance(self.cursor, 1, W.cap, self.idx_one, self.kv_len)
+            skv.kv_write_indexed(self.kc, self.vc, self.k_steps[i], self.v_steps[i], index=self.idx_one)
+            if events is not None:
+                events[i][0].record()
+            skv.attn_chunk_fwd(self.q_steps[i], self.kc, self.vc, self.out[i], kv_len_dev=self.kv_len,
+                               max_seqlen_kv=self.max_kv, workspace=self.ws)
+            if events is not None:
+                events[i][1].record()
+
+
+def bench_decode(torch, skv, SI, dev, args):
+    job = DecodeJob(torch, skv, SI, dev, args.dtype)
+    # eager warm-up (also builds every kernel), then record the job into a graph
+    job.run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        job.run()  # one more eager run on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        job.run()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = event_pair(torch)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    gpu_ms = e0.elapsed_time(e1) / args.steps
+
+    # per-launch duration of the decode attention kernel: events around each launch, with the
+    # whole job enqueued behind a GPU-side sleep so host launch gaps do not enter the pairs
+    events = [event_pair(torch) for _ in range(job.W.steps)]
+    t_host = time.perf_counter()
+    job.run(events)  # host time to enqueue one job with its events
+    t_host = time.perf_counter() - t_host
+    torch.cuda.synchronize()
+    a, b = event_pair(torch)
+    a.record()
+    torch.cuda._sleep(10_000_000)
+    b.record()
+    b.synchronize()
+    sleep_cycles = int(10_000_000 * max(2.0 * t_host * 1e3, 20.0) / max(a.elapsed_time(b), 1e-3))
+    durations = []
+    for rep in range(3):
+        torch.cuda._sleep(sleep_cycles)  # the GPU waits while the host enqueues the whole job
+        job.run(events)
+        torch.cuda.synchronize()
+        durations.append([a.elapsed_time(b) for a, b in events])
+    per_launch = [statistics.median(d[i] for d in durations) for i in range(job.W.steps)]
+    mean_ms = sum(per_launch) / len(per_launch)
+    mean_bytes = sum(job.decode_launch_bytes) / len(job.decode_launch_bytes)
+    achieved = mean_bytes / (mean_ms * 1e-3) / 1e9
+    return {
+        "job": job,
+        "ms_per_step": wall * 1e3,
+        "gpu_ms_per_step": gpu_ms,
+        "value": job.kv_bytes_job / wall / 1e9,
+        "decode_kernel": {"mean_us": mean_ms * 1e3, "mean_bytes": mean_bytes, "achieved_gbs": achieved,
+                          "first_us": per_launch[0] * 1e3, "last_us": per_launch[-1] * 1e3},
+        "decode_steps_per_s": job.W.steps / wall,
+    }
+
+
+# ----------------------------------------------------------------------------------------
+# other hot-path workloads (reported under "rows")
+# ----------------------------------------------------------------------------------------
+def bench_ring(torch, skv, SI, dev):
+    W = SI.Ring()
+    rows = W.n_slots * W.C
+    ks = torch.zeros(W.B, rows, W.H, W.D, dtype=torch.bfloat16, device=dev)
+    vs = torch.zeros_like(ks)
+    ring = skv.Ring(ks, vs, W.C, W.n_slots, W.sink)
+    shape = (W.C, W.H, W.D)
+    srcs = [(SI.per_batch_device_normal(W.B, shape, "ring", "q", dev, "bf16", chunk=c, rewrite=r),
+             SI.per_batch_device_normal(W.B, shape, "ring", "k", dev, "bf16", chunk=c, rewrite=r),
+             SI.per_batch_device_normal(W.B, shape, "ring", "v", dev, "bf16", chunk=c, rewrite=r))
+            for c in range(2) for r in range(2)]
+    out = torch.empty(W.B, W.C, W.H, W.D, dtype=torch.bfloat16, device=dev)
+
+    def sequence():
+        ring.reset()
+        for c in range(W.n_chunks):
+            ring.reserve()
+            for r in range(W.rewrites):
+                q, k, v = srcs[(c % 2) * 2 + (r % 2)]
+                ring.write(k, v)
+                skv.attn_chunk_fwd(q, ks, vs, out, kv_len_dev=ring.kv_len, max_seqlen_kv=rows)
+
+    seq_ms = time_gpu(torch, sequence, reps=3, warm=1)
+    # saturated step: 7 valid slots
+    ring.reset()
+    for c in range(W.n_slots):
+        ring.reserve()
+        ring.write(srcs[0][1], srcs[0][2])
+    q = srcs[1][0]
+    attn_ms = time_gpu(torch, lambda: skv.attn_chunk_fwd(q, ks, vs, out, kv_len_dev=ring.kv_len,
+                                                         max_seqlen_kv=rows), reps=10)
+    flush = make_flush(torch, dev)
+    write_ms = time_gpu(torch, lambda: ring.write(srcs[0][1], srcs[0][2]), reps=10, flush=flush)
+    del flush
+    reset_ms = time_gpu(torch, lambda: ring.reset(), reps=10)
+    flop_sat = 4 * W.D * W.H * W.B * W.C * (W.n_slots * W.C)
+    flop_seq = sum(4 * W.D * W.H * W.B * W.C * (min(c + 1, W.n_slots) * W.C) * W.rewrites
+                   for c in range(W.n_chunks))
+    wbytes = 2 * 2 * W.B * W.C * W.H * W.D * ELEM
+    return {
+        "workload": "ring: B=2, 12 heads, D=128, bf16, chunks of 4680, 7 slots (1 sink), 12 chunks x 4 rewrites",
+        "sequence_ms": seq_ms, "sequence_tflops": flop_seq / seq_ms * 1e-9,
+        "ms_per_rewrite_step": seq_ms / (W.n_chunks * W.rewrites),
+        "saturated_attn_ms": attn_ms, "saturated_attn_tflops": flop_sat / attn_ms * 1e-9,
+        "saturated_attn_frac_mfma": flop_sat / attn_ms * 1e-9 / MFMA_BF16_PEAK_TFS,
+        "ring_write_ms_cold": write_ms, "ring_write_gbs": wbytes / write_ms * 1e-6,
+        "ring_write_frac_hbm": wbytes / write_ms * 1e-6 / HBM_PEAK_GBS,
+        "reset_us": reset_ms * 1e3,
+    }
+
+
+def bench_multiuser(torch, skv, SI, dev):
+    W = SI.MultiUser()
+    kc = torch.zeros(W.B, W.cap, W.H, W.D, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    shape = (W.chunk, W.H, W.D)
+    q = SI.per_batch_device_normal(W.B, shape, "multiuser", "q", dev, "bf16")
+    k = SI.per_batch_device_normal(W.B, shape, "multiuser", "k", dev, "bf16")
+    v = SI.per_batch_device_normal(W.B, shape, "multiuser", "v", dev, "bf16")
+    cursor = torch.zeros(1, dtype=torch.int32, device=dev)
+    kv_len = torch.zeros(W.B, dtype=torch.int32, device=dev)
+    idx = torch.empty(W.chunk, dtype=torch.int64, device=dev)
+    out = torch.empty_like(q)
+
+    def sequence():
+        cursor.zero_()
+        for c in range(W.n_chunks):
+            skv.kv_cursor_advance(cursor, W.chunk, W.cap, idx, kv_len)
+            skv.kv_write_indexed(kc, vc, k, v, index=idx)
+            skv.attn_chunk_fwd(q, kc, vc, out, kv_len_dev=kv_len, mask=skv.MASK_BLOCK_CAUSAL,
+                               mask_block=W.block, max_seqlen_kv=W.cap)
+
+    seq_ms = time_gpu(torch, sequence, reps=3, warm=1)
+    last = W.cap
+    c15_ms = time_gpu(torch, lambda: skv.attn_chunk_fwd(q, kc, vc, out, kv_len=last, mask=skv.MASK_BLOCK_CAUSAL,
+                                                        mask_block=W.block), reps=10)
+    flush = make_flush(torch, dev)
+    index = torch.arange(W.cap - W.chunk, W.cap, device=dev)
+    write_ms = time_gpu(torch, lambda: skv.kv_write_indexed(kc, vc, k, v, index=index), reps=10, flush=flush)
+    del flush
+    pairs = lambda c: W.chunk * (W.chunk * c) + W.chunk * (W.chunk + 1) // 2  # noqa: E731 (block 1)
+    flop_seq = sum(4 * W.D * W.H * W.B * pairs(c) for c in range(W.n_chunks))
+    flop_c15 = 4 * W.D * W.H * W.B * pairs(W.n_chunks - 1)
+    wbytes = 2 * 2 * W.B * W.chunk * W.H * W.D * ELEM
+    return {
+        "workload": "multi-user slab: B=8, 40 heads, D=128, bf16, cap 16384, 16 chunks of 1024, causal in chunk",
+        "sequence_ms": seq_ms, "sequence_tflops": flop_seq / seq_ms * 1e-9,
+        "ms_per_chunk_step": seq_ms / W.n_chunks,
+        "chunk15_attn_ms": c15_ms, "chunk15_attn_tflops": flop_c15 / c15_ms * 1e-9,
+        "chunk15_attn_frac_mfma": flop_c15 / c15_ms * 1e-9 / MFMA_BF16_PEAK_TFS,
+        "slab_write_ms_cold": write_ms, "slab_write_gbs": wbytes / write_ms * 1e-6,
+        "slab_write_frac_hbm": wbytes / write_ms * 1e-6 / HBM_PEAK_GBS,
+    }
+
+
+def bench_ragged(torch, skv, SI, dev):
+    W = SI.Ragged()
+    q = SI.per_batch_device_normal(W.B, (W.Tq, W.H, W.D), "ragged", "q", dev, "bf16")
+    out = torch.empty_like(q)
+    res = {"workload": "ragged cross-attention: 2 branches, 40 heads, D=128, bf16, Q 75600 per branch"}
+    for lens in W.skews:
+        total = sum(lens)
+        kp = SI.device_normal((total, W.H, W.D), SI.seed_key("ragged", "k", 0, lens[1]), "bf16", dev)
+        vp = SI.device_normal((total, W.H, W.D), SI.seed_key("ragged", "v", 0, lens[1]), "bf16", dev)
+        cu = torch.tensor([0, lens[0], total], dtype=torch.int32, device=dev)
+        kpad = torch.zeros(W.B, W.max_kv, W.H, W.D, dtype=torch.bfloat16, device=dev)
+        vpad = torch.zeros_like(kpad)
+        kpad[0, :lens[0]], kpad[1, :lens[1]] = kp[:lens[0]], kp[lens[0]:]
+        vpad[0, :lens[0]], vpad[1, :lens[1]] = vp[:lens[0]], vp[lens[0]:]
+        used = torch.tensor(list(lens), dtype=torch.int32, device=dev)
+        arms = {
+            "packed": lambda: skv.attn_chunk_fwd(q, kp, vp, out, cu_seqlens_kv=cu, max_seqlen_kv=W.max_kv),
+            "seqused": lambda: skv.attn_chunk_fwd(q, kpad, vpad, out, kv_len_dev=used, max_seqlen_kv=W.max_kv),
+            "padded_masked": lambda: skv.attn_chunk_fwd(q, kpad, vpad, out, kv_len_dev=used, max_seqlen_kv=W.max_kv,
+                                                        full_capacity_masked=True),
+        }
+        flop = 4 * W.D * W.H * W.Tq * total
+        byts = 2 * W.B * W.Tq * W.H * W.D * ELEM + 2 * total * W.H * W.D * ELEM
+        entry = {}
+        for name, fn in arms.items():
+            ms = time_gpu(torch, fn, reps=10)
+            entry[name] = {"ms": ms, "tflops": flop / ms * 1e-9, "gbs": byts / ms * 1e-6,
+                           "roofline_frac": max(flop / ms * 1e-9 / MFMA_BF16_PEAK_TFS,
+                                                byts / ms * 1e-6 / HBM_PEAK_GBS)}
+        res[f"{lens[0]},{lens[1]}"] = entry
+    return res
+
+
+def bench_sweep(torch, skv, SI, dev):
+    W = SI.Decode()
+    kc = SI.device_normal((1, W.cap, W.Hkv, W.D), SI.seed_key("decode", "k", 0, 7), "bf16", dev, std=W.std)
+    vc = SI.device_normal((1, W.cap, W.Hkv, W.D), SI.seed_key("decode", "v", 0, 7), "bf16", dev, std=W.std)
+    q = SI.device_normal((1, 1, W.Hq, W.D), SI.seed_key("decode", "q", 0, 7), "bf16", dev, std=W.std)
+    out = torch.empty_like(q)
+    ws = torch.zeros(skv.attn_workspace_bytes(q, kc, kv_len=W.cap, full_capacity_masked=True),
+                     dtype=torch.uint8, device=dev)  # the largest split count of the sweep
+    flush = make_flush(torch, dev)
+    res = {"workload": "decode attention alone, B=1, 32/8 heads, D=128, bf16, cold L2 and Infinity Cache"}
+    for L in (1258, 4096, 8192, 16384, 32768):
+        ms = time_gpu(torch, lambda: skv.attn_chunk_fwd(q, kc, vc, out, kv_len=L, workspace=ws), reps=10,
+                      flush=flush)
+        byts = 2 * L * W.Hkv * W.D * ELEM + 2 * W.Hq * W.D * ELEM
+        res[str(L)] = {"us": ms * 1e3, "gbs": byts / ms * 1e-6, "frac_hbm": byts / ms * 1e-6 / HBM_PEAK_GBS}
+    ms = time_gpu(torch, lambda: skv.attn_chunk_fwd(q, kc, vc, out, kv_len=1258, full_capacity_masked=True,
+                                                    workspace=ws), reps=10, flush=flush)
+    byts = 2 * W.cap * W.Hkv * W.D * ELEM
+    res["full_capacity_arm_kv1258"] = {"us": ms * 1e3, "gbs_visited": byts / ms * 1e-6,
+                                       "slowdown_vs_active": ms * 1e3 / res["1258"]["us"]}
+    return res
+
+
+# ----------------------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the decode job
+# ----------------------------------------------------------------------------------------
+def cpu_baseline(SI, dtype, n_steps=40):
+    import numpy as np
+    from oracle import attention as A
+    from oracle import cache as Cc
+    W = SI.Decode()
+    n = W.prompt + n_steps
+    q = SI.as_f64(SI.per_batch_normal(1, (n, W.Hq, W.D), "decode", "q", std=W.std, dtype=dtype))[0]
+    k = SI.as_f64(SI.per_batch_normal(1, (n, W.Hkv, W.D), "decode", "k", std=W.std, dtype=dtype))
+    v = SI.as_f64(SI.per_batch_normal(1, (n, W.Hkv, W.D), "decode", "v", std=W.std, dtype=dtype))
+    T = W.prompt
+    t0 = time.perf_counter()
+    kc, _ = Cc.slab_write_indexed(np.zeros((1, W.cap, W.Hkv, W.D)), k[:, :T], np.arange(T))
+    vc, _ = Cc.slab_write_indexed(np.zeros((1, W.cap, W.Hkv, W.D)), v[:, :T], np.arange(T))
+    A.attend_prefix(q[:T], kc[0], vc[0], T, A.MASK_CAUSAL)
+    for i in range(n_steps):
+        kc, _ = Cc.slab_write_indexed(kc, k[:, T + i:T + i + 1], [T + i])
+        vc, _ = Cc.slab_write_indexed(vc, v[:, T + i:T + i + 1], [T + i])
+        A.attend_prefix(q[T + i:T + i + 1], kc[0], vc[0], T + i + 1)
+    secs = time.perf_counter() - t0
+    kv_bytes = 2 * T * W.Hkv * W.D * ELEM + sum(2 * (T + i + 1) * W.Hkv * W.D * ELEM for i in range(n_steps))
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return {"value": kv_bytes / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": secs, "host_cpus": os.cpu_count(),
+            "sample": f"prefill (234-token causal) + first {n_steps} of 1024 decode steps, "
+                      f"fp64 numpy oracle incl. its slab writes (capacity 32768)"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_decode.hip", "common.h"):
+        with open(os.path.join(ROOT, "streaming_kv_cache_write_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "decode_attention_counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import seeded_inputs as SI
+    import streaming_kv_cache_write_amd as skv
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.only and args.only != "decode":
+        fn = {"ring": bench_ring, "multiuser": bench_multiuser, "ragged": bench_ragged,
+              "sweep": bench_sweep}[args.only]
+        print(json.dumps({args.only: fn(torch, skv, SI, dev)}))
+        return
+
+    d = bench_decode(torch, skv, SI, dev, args)
+    dk = d["decode_kernel"]
+    line = {
+        "metric": "chunk-attn TFLOP/s + decode KV-read GB/s (% of MI355X peak); ms per chunk step",
+        "value": round(d["value"], 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": "decode with active prefix: B=1, 32 q heads / 8 kv heads, D=128, "
+                               "capacity 32768, 234-token causal prefill + 1024 single-token steps "
+                               "(kv_len 235..1258); one step = the whole job, replayed as a HIP graph",
+                   "decode_steps_per_s": round(d["decode_steps_per_s"], 1),
+                   "gpu_ms_per_step": round(d["gpu_ms_per_step"], 4)},
+        "roofline": {"bound": "hbm", "achieved": round(dk["achieved_gbs"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dk["achieved_gbs"] / HBM_PEAK_GBS, 5),
+                     "traffic": traffic_from_profile(),
+                     "kernel": "k_attn_decode (split-K decode attention, fused merge)",
+                     "mean_launch_us": round(dk["mean_us"], 3),
+                     "algorithmic_bytes_per_launch": round(dk["mean_bytes"])},
+    }
+    if not args.no_rows:
+        rows = {}
+        for name, fn in (("ring", bench_ring), ("multiuser", bench_multiuser), ("ragged", bench_ragged),
+                         ("decode_sweep", bench_sweep)):
+            try:
+                rows[name] = fn(torch, skv, SI, dev)
+            except Exception as e:  # report, never hide
+                rows[name] = {"error": repr(e)}
+            torch.cuda.empty_cache()
+        line["rows"] = rows
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(SI, args.dtype)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

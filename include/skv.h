@@ -166,9 +166,11 @@ skv_status kv_ring_destroy(skv_ring* ring);
  * fp32 accumulation and fp32 softmax). out_dtype: dtype or SKV_F32.
  * Tq <= 4 (decode-sized chunks) in bf16/f16 uses a split-K path that needs a workspace of
  * attn_workspace_bytes(params) bytes (caller device memory, 16-byte aligned); other shapes
- * need none. The workspace must be zero-filled once before its first use (it holds arrival
- * counters that every call leaves at zero again); calls sharing one workspace must not
- * overlap in time (they are ordered when issued on one stream).
+ * need none. The workspace must be zero-filled once before its first use: its first bytes
+ * hold arrival counters (B*Hkv int32, at offset 0 whatever the split count) that every call
+ * leaves at zero again, so one zero-filled workspace of the largest size needed can serve
+ * every later call. Calls sharing one workspace must not overlap in time (they are ordered
+ * when issued on one stream).
  * max_seqlen_kv: optional host bound on any batch element's key count; it only sizes the
  * split-K grid when the lengths live on the device (0 = use cap / the host kv_len).
  * ------------------------------------------------------------------------------------ */

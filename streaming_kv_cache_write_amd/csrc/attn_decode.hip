@@ -35,6 +35,9 @@ template <> struct Mfma16<f16_t> {
 constexpr int kDecBN = 64;   // keys per tile
 constexpr int kDecRows = 16; // row slots per (b, KV head) in the workspace
 
+__host__ __device__ __forceinline__ size_t dec_counter_floats(int B, int Hkv) {
+  return (((size_t)B * Hkv + 63) / 64) * 64;  // 256-byte multiple
+}
 __host__ __device__ __forceinline__ size_t dec_o_floats(int B, int Hkv, int D, int n_splits) {
   return (size_t)B * Hkv * kDecRows * n_splits * D;
 }
@@ -108,9 +111,10 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
   const int lane = threadIdx.x;
   const int col = lane & 15, quad = lane >> 4;
   const int R = a.Tq * group;
-  float* ws_o = ws;
-  float* ws_ml = ws + dec_o_floats(a.B, a.Hkv, D, n_splits);
-  int* counters = (int*)(ws_ml + dec_ml_floats(a.B, a.Hkv, n_splits));
+  // workspace: arrival counters first (a fixed place for any split count), then partials
+  int* counters = (int*)ws;
+  float* ws_o = ws + dec_counter_floats(a.B, a.Hkv);
+  float* ws_ml = ws_o + dec_o_floats(a.B, a.Hkv, D, n_splits);
 
   // a rejected batch element still takes part in the arrival count, with empty splits
   const KeySet ks = key_set(a, b);
@@ -316,8 +320,8 @@ int decode_splits(int B, int Hkv, int max_len) {
 }
 
 size_t decode_workspace_bytes(int B, int Hkv, int D, int n_splits) {
-  return (dec_o_floats(B, Hkv, D, n_splits) + dec_ml_floats(B, Hkv, n_splits)) * sizeof(float) +
-         (size_t)B * Hkv * sizeof(int);
+  return (dec_counter_floats(B, Hkv) + dec_o_floats(B, Hkv, D, n_splits) +
+          dec_ml_floats(B, Hkv, n_splits)) * sizeof(float);
 }
 
 template <typename T, int D, typename OutT>
