@@ -89,7 +89,8 @@ def make_flush(torch, dev):
 class DecodeJob:
     """Prefill + 1024 decode steps through the device cursor; everything device-resident."""
 
-    def __init__(self, torch, skv, SI, dev, dtype):
+    def __init__(self, torch, skv, SI, dev, dtype, fused=True):
+        self.fused = fused
         W = SI.Decode()
         self.W, self.torch, self.skv = W, torch, skv
         n = W.prompt + W.steps
@@ -108,9 +109,8 @@ class DecodeJob:
         T = W.prompt
         # the job's longest prefix bounds the split-K grid (device kv_len, fixed launch shape)
         self.max_kv = T + W.steps
-        self.ws = torch.zeros(skv.attn_workspace_bytes(self.q[:, T:T + 1], self.kc, kv_len_dev=self.kv_len,
-                                                       max_seqlen_kv=self.max_kv), dtype=torch.uint8,
-                              device=dev)
+        self.ws = torch.zeros(skv.attn_workspace_bytes(self.q[:, T:T + 1], self.kc, kv_len=self.max_kv),
+                              dtype=torch.uint8, device=dev)
         # prebuilt views so the replayed sequence does no tensor bookkeeping
         self.q_pre, self.k_pre, self.v_pre = self.q[:, :T], self.k[:, :T], self.v[:, :T]
         self.q_steps = [self.q[:, T + i:T + i + 1] for i in range(W.steps)]
@@ -130,6 +130,15 @@ class DecodeJob:
         skv.attn_chunk_fwd(self.q_pre, self.kc, self.vc, self.out_pre, kv_len_dev=self.kv_len,
                            mask=skv.MASK_CAUSAL, max_seqlen_kv=W.cap)
         for i in range(W.steps):
+            if self.fused:  # one launch: cursor read, row write, attention, cursor advance
+                if events is not None:
+                    events[i][0].record()
+                skv.attn_decode_step(self.q_steps[i], self.k_steps[i], self.v_steps[i], self.kc, self.vc,
+                                     self.cursor, self.out[i], kv_len_out=self.kv_len,
+                                     max_seqlen_kv=self.max_kv, workspace=self.ws)
+                if events is not None:
+                    events[i][1].record()
+                continue
             skv.kv_cursor_advance(self.cursor, 1, W.cap, self.idx_one, self.kv_len)
             skv.kv_write_indexed(self.kc, self.vc, self.k_steps[i], self.v_steps[i], index=self.idx_one)
             if events is not None:
@@ -140,8 +149,8 @@ class DecodeJob:
                 events[i][1].record()
 
 
-def bench_decode(torch, skv, SI, dev, args):
-    job = DecodeJob(torch, skv, SI, dev, args.dtype)
+def bench_decode(torch, skv, SI, dev, args, fused=True):
+    job = DecodeJob(torch, skv, SI, dev, args.dtype, fused)
     # eager warm-up (also builds every kernel), then record the job into a graph
     job.run()
     torch.cuda.synchronize()
@@ -449,17 +458,26 @@ def main():
         "config": {"workload": "decode with active prefix: B=1, 32 q heads / 8 kv heads, D=128, "
                                "capacity 32768, 234-token causal prefill + 1024 single-token steps "
                                "(kv_len 235..1258); one step = the whole job, replayed as a HIP graph",
+                   "decode_step": "fused attn_decode_step (cursor read + row write + split-K attention "
+                                  "+ cursor advance in one launch)",
                    "decode_steps_per_s": round(d["decode_steps_per_s"], 1),
                    "gpu_ms_per_step": round(d["gpu_ms_per_step"], 4)},
         "roofline": {"bound": "hbm", "achieved": round(dk["achieved_gbs"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dk["achieved_gbs"] / HBM_PEAK_GBS, 5),
                      "traffic": traffic_from_profile(),
-                     "kernel": "k_attn_decode (split-K decode attention, fused merge)",
+                     "kernel": "k_attn_decode, fused step (row write + split-K attention + merge)",
                      "mean_launch_us": round(dk["mean_us"], 3),
                      "algorithmic_bytes_per_launch": round(dk["mean_bytes"])},
     }
     if not args.no_rows:
         rows = {}
+        u = bench_decode(torch, skv, SI, dev, args, fused=False)
+        rows["decode_three_calls"] = {
+            "workload": "same decode job with kv_cursor_advance + kv_write_indexed + attn_chunk_fwd per step",
+            "ms_per_job": u["ms_per_step"], "kv_read_gbs": u["value"],
+            "attn_kernel_mean_us": u["decode_kernel"]["mean_us"]}
+        del u
+        torch.cuda.empty_cache()
         for name, fn in (("ring", bench_ring), ("multiuser", bench_multiuser), ("ragged", bench_ragged),
                          ("decode_sweep", bench_sweep)):
             try:

@@ -205,6 +205,27 @@ size_t attn_workspace_bytes(const skv_attn_params* params);
 skv_status attn_chunk_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                           const skv_attn_params* params, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Fused decode step [FS, Change: decode step i writes position T+i and attends over
+ * kv_len = T+i+1] [LB, What this is and isn't; FD, proposed boundary: positions on the device]
+ *
+ * One launch with the effect of kv_cursor_advance(cursor_dev, Tq, cap, ...) +
+ * kv_write_indexed(k_cache, v_cache, k_new, v_new, index) + attn_chunk_fwd(q, k_cache, v_cache,
+ * kv_len_dev = the advanced lengths): c = *cursor_dev; for every batch element b the new rows
+ * k_new/v_new [B, Tq, Hkv, D] are stored at cache rows c .. c+Tq-1 of k_cache/v_cache
+ * [B, cap, Hkv, D]; out = attention of q [B, Tq, Hq, D] over rows [0, c+Tq) (params->mask
+ * applies, queries bottom-right aligned); then *cursor_dev = c+Tq and, if non-NULL,
+ * kv_len_out_dev[b] = c+Tq. If c+Tq > cap nothing is written, the cursor stays, outputs are
+ * zero and SKV_DEV_CURSOR_FULL is set. Outputs equal the three-call sequence bit for bit.
+ * params: prefix mode with kv_len_dev = cu_seqlens_kv_dev = NULL and no full-capacity flag
+ * (SKV_ERR_UNSUPPORTED otherwise); params->kv_len is ignored; bf16/f16 with Tq <= 4 and
+ * Tq*Hq/Hkv <= 16. The workspace follows attn_workspace_bytes() of the same params (zero-filled
+ * before first use, left zero-filled); max_seqlen_kv bounds c+Tq for grid sizing (0 = cap).
+ * ------------------------------------------------------------------------------------ */
+skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                            void* v_cache, void* out, float* lse, int32_t* cursor_dev,
+                            int32_t* kv_len_out_dev, const skv_attn_params* params, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libskv.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m streaming_kv_cache_write_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python streaming_kv_cache_write_amd/build.py`")
 lib = ctypes.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------------------ constants
@@ -71,6 +71,8 @@ _SIGS = {
     "kv_ring_destroy": (_i, [_vp]),
     "attn_workspace_bytes": (_sz, [ctypes.POINTER(skv_attn_params)]),
     "attn_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, ctypes.POINTER(skv_attn_params), _vp]),
+    "attn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                              ctypes.POINTER(skv_attn_params), _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -284,4 +286,38 @@ def attn_chunk_fwd(q, k, v, out=None, lse=None, *, kv_len=None, kv_len_dev=None,
     p = make_params(q, k, workspace=workspace, **kw)
     _check(lib.attn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), ctypes.byref(p),
                               _stream(q.device)))
+    return out
+
+
+def attn_decode_step(q, k_new, v_new, k_cache, v_cache, cursor, out=None, lse=None, *,
+                     kv_len_out=None, max_seqlen_kv=0, mask=MASK_NONE, mask_block=1, scale=0.0,
+                     out_dtype=None, workspace=None, err=None):
+    """One fused decode step: write k_new/v_new [B, Tq, Hkv, D] at the device cursor, attend q
+    [B, Tq, Hq, D] over the cache prefix including them, advance the cursor (and fill
+    kv_len_out [B]). Returns out."""
+    _dev_tensor(q, "q")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev_tensor(t, name, q.dtype)
+    _dev_tensor(cursor, "cursor", torch.int32)
+    if kv_len_out is not None:
+        _dev_tensor(kv_len_out, "kv_len_out", torch.int32)
+    if err is not None:
+        _dev_tensor(err, "err", torch.int32)
+    odt = out_dtype if out_dtype is not None else q.dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=odt, device=q.device)
+    _dev_tensor(out, "out", odt)
+    if lse is not None:
+        _dev_tensor(lse, "lse", torch.float32)
+    bound = int(max_seqlen_kv) if max_seqlen_kv else k_cache.shape[1]
+    kw = dict(max_seqlen_kv=max_seqlen_kv, mask=mask, mask_block=mask_block, scale=scale,
+              out_dtype=odt, err=err)
+    if workspace is None:
+        need = attn_workspace_bytes(q, k_cache, kv_len=min(bound, k_cache.shape[1]), **kw)
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev_tensor(workspace, "workspace")
+    p = make_params(q, k_cache, workspace=workspace, **kw)
+    _check(lib.attn_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(out), _ptr(lse), _ptr(cursor), _ptr(kv_len_out), ctypes.byref(p),
+                                _stream(q.device)))
     return out

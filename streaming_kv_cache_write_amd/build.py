@@ -1,6 +1,7 @@
 """Compile libskv.so (the HIP kernels and the C ABI of include/skv.h) for gfx950, in tree.
 
-Usage: python -m streaming_kv_cache_write_amd.build   (or call build()).
+Usage: python streaming_kv_cache_write_amd/build.py   (a script: importing the package would
+load the library this builds).
 Every call recompiles; objects go to _build/ beside this file, the library to libskv.so.
 """
 from __future__ import annotations

@@ -244,7 +244,7 @@ skv_status attn_chunk_fwd(const void* q, const void* k, const void* v, void* out
   if (st != SKV_OK) return st;
   if (lse && ((uintptr_t)lse & 3)) return fail(SKV_ERR_ALIGN, "lse must be 4-byte aligned");
   if (p->Tq == 0) return ok();
-  AttnArgs a;
+  AttnArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -283,6 +283,59 @@ skv_status attn_chunk_fwd(const void* q, const void* k, const void* v, void* out
     }
   }
   return fail(SKV_ERR_UNSUPPORTED, "no path");
+}
+
+skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                            void* v_cache, void* out, float* lse, int32_t* cursor_dev,
+                            int32_t* kv_len_out_dev, const skv_attn_params* p, void* stream) {
+  if (!p) return fail(SKV_ERR_NULL, "params is NULL");
+  if (!k_new || !v_new || !cursor_dev) return fail(SKV_ERR_NULL, "k_new, v_new and cursor_dev must be non-NULL");
+  if (p->kv_len_dev || p->cu_seqlens_kv_dev || (p->flags & SKV_FULL_CAPACITY_MASKED))
+    return fail(SKV_ERR_UNSUPPORTED, "the fused decode step takes its length from the cursor "
+                                     "(no kv_len_dev, cu_seqlens_kv_dev or full-capacity arm)");
+  skv_attn_params v = *p;
+  v.kv_len = v.cap;  // any valid host length: the kernel reads the cursor instead
+  if (v.mask != SKV_MASK_NONE && v.Tq > v.kv_len) v.kv_len = v.Tq;
+  skv_status st = validate_attn(q, k_cache, v_cache, out, &v);
+  if (st != SKV_OK) return st;
+  if (p->Tq == 0) return ok();
+  if (choose_path(v) != PATH_DECODE)
+    return fail(SKV_ERR_UNSUPPORTED, "the fused decode step needs bf16/f16, Tq <= %d and "
+                "Tq*Hq/Hkv <= %d", kDecodeMaxTq, kDecodeMaxRows);
+  if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)cursor_dev & 3) ||
+      ((uintptr_t)kv_len_out_dev & 3) || (lse && ((uintptr_t)lse & 3)))
+    return fail(SKV_ERR_ALIGN, "misaligned k_new / v_new / cursor / kv_len_out / lse");
+  v.kv_len_dev = nullptr;
+  const int splits = decode_splits(p->B, p->Hkv, p->max_seqlen_kv > 0 && p->max_seqlen_kv < p->cap
+                                                     ? p->max_seqlen_kv : p->cap);
+  const size_t need = decode_workspace_bytes(p->B, p->Hkv, p->D, splits);
+  if (!p->workspace) return fail(SKV_ERR_NULL, "the decode step needs a workspace of %zu bytes", need);
+  if (p->workspace_bytes < need)
+    return fail(SKV_ERR_RANGE, "workspace of %zu bytes < %zu required", p->workspace_bytes, need);
+  if (!aligned16(p->workspace)) return fail(SKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  AttnArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.lse = lse;
+  a.err = p->err_dev;
+  a.B = p->B;
+  a.Tq = p->Tq;
+  a.Hq = p->Hq;
+  a.Hkv = p->Hkv;
+  a.cap = p->cap;
+  a.mask = p->mask;
+  a.block = p->mask == SKV_MASK_BLOCK_CAUSAL ? p->mask_block : 1;
+  a.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->D);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cursor = cursor_dev;
+  a.kv_len_out = kv_len_out_dev;
+  return hip_status(launch_attn_decode(a, p->dtype, p->out_dtype, p->D, p->workspace, splits,
+                                       (hipStream_t)stream),
+                    "attn_decode_step launch");
 }
 
 }  // extern "C"

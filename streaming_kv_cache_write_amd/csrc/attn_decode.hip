@@ -36,7 +36,7 @@ constexpr int kDecBN = 64;   // keys per tile
 constexpr int kDecRows = 16; // row slots per (b, KV head) in the workspace
 
 __host__ __device__ __forceinline__ size_t dec_counter_floats(int B, int Hkv) {
-  return (((size_t)B * Hkv + 63) / 64) * 64;  // 256-byte multiple
+  return (((size_t)B * Hkv + 1 + 63) / 64) * 64;  // B*Hkv split counters + 1, 256-byte multiple
 }
 __host__ __device__ __forceinline__ size_t dec_o_floats(int B, int Hkv, int D, int n_splits) {
   return (size_t)B * Hkv * kDecRows * n_splits * D;
@@ -57,49 +57,79 @@ __device__ __forceinline__ void unpack8(const uint4& u, float* f) {
   for (int i = 0; i < 8; ++i) f[i] = to_f32(e[i]);
 }
 
-// Merge the n_splits partials of row r of (b, g) and write the output row:
-// weights exp2((m_s - M) * scale * log2 e), M = max_s m_s.
+// Merge the n_splits partials of the R rows of (b, g) and write the output rows. Lane layout:
+// row r0 + lane/16 of each pass of 4 rows, columns [8*(lane%16), +8). One online pass over the
+// splits (running max M, weights exp2((m_s - M) * scale * log2 e)); the loads of 8 splits are
+// issued together and nothing in the loop branches on loaded data.
 template <int D, typename OutT>
-__device__ __forceinline__ void merge_row(const AttnArgs& a, int group, const float* ws_o,
-                                          const float* ws_ml, int b, int g, int r, int n_splits,
-                                          int lane) {
-  const int t = r / group, h = g * group + (r - t * group);
-  const size_t p0 = dec_part_index(b, g, r, 0, a.Hkv, n_splits);
+__device__ __forceinline__ void merge_rows(const AttnArgs& a, int group, const float* ws_o,
+                                           const float* ws_ml, int b, int g, int R, int n_splits,
+                                           int lane) {
+  constexpr int kBatch = 8;
+  const int dc = lane & 15;
+  const bool col_ok = dc < D / 8;
   const float c2 = a.scale_log2;
-  float M = -INFINITY;
-  for (int s = lane; s < n_splits; s += 64) M = fmaxf(M, ws_ml[2 * (p0 + s)]);
+  for (int r0 = 0; r0 < R; r0 += 4) {
+    const int r = r0 + (lane >> 4);
+    const bool row_ok = r < R;
+    const size_t p0 = dec_part_index(b, g, row_ok ? r : 0, 0, a.Hkv, n_splits);
+    float M = -INFINITY, L = 0.f;
+    float o[8];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  OutT* out = (OutT*)a.out + (((int64_t)b * a.Tq + t) * a.Hq + h) * D;
-  if (M == -INFINITY) {  // no visible key at all (the batch element was rejected)
-    for (int d = lane; d < D; d += 64) out[d] = from_f32<OutT>(0.f);
-    if (a.lse && lane == 0) a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = -INFINITY;
-    return;
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+      float2 ml[kBatch];
+      float4 oa[kBatch], ob[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int sp = s0 + u;
+        const bool ok = sp < n_splits;
+        ml[u] = ok ? *(const float2*)(ws_ml + 2 * (p0 + sp)) : make_float2(-INFINITY, 0.f);
+        const float* po = ws_o + (p0 + (ok ? sp : 0)) * D + 8 * dc;
+        oa[u] = (ok && col_ok) ? *(const float4*)po : make_float4(0.f, 0.f, 0.f, 0.f);
+        ob[u] = (ok && col_ok) ? *(const float4*)(po + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float m_new = fmaxf(M, ml[u].x);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float wa = __builtin_amdgcn_exp2f((M - m_use) * c2);       // rescale of the sum so far
+        const float wb = __builtin_amdgcn_exp2f((ml[u].x - m_use) * c2); // weight of split s
+        L = L * wa + ml[u].y * wb;
+        o[0] = o[0] * wa + oa[u].x * wb;
+        o[1] = o[1] * wa + oa[u].y * wb;
+        o[2] = o[2] * wa + oa[u].z * wb;
+        o[3] = o[3] * wa + oa[u].w * wb;
+        o[4] = o[4] * wa + ob[u].x * wb;
+        o[5] = o[5] * wa + ob[u].y * wb;
+        o[6] = o[6] * wa + ob[u].z * wb;
+        o[7] = o[7] * wa + ob[u].w * wb;
+        M = m_new;
+      }
+    }
+    if (!row_ok) continue;
+    const int t = r / group, h = g * group + (r - t * group);
+    OutT* out = (OutT*)a.out + (((int64_t)b * a.Tq + t) * a.Hq + h) * D + 8 * dc;
+    const float inv = L > 0.f ? 1.f / L : 0.f;  // L = 0: the batch element was rejected
+    if (col_ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = from_f32<OutT>(o[e] * inv);
+    }
+    if (a.lse && dc == 0)
+      a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = L > 0.f ? M * a.scale + logf(L) : -INFINITY;
   }
-  float L = 0.f;
-  float o[D / 64];
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < n_splits; ++s) {
-    const float ms = ws_ml[2 * (p0 + s)];
-    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ms - M) * c2);
-    L = fmaf(w, ws_ml[2 * (p0 + s) + 1], L);
-    const float* po = ws_o + (p0 + s) * D;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) o[i] = fmaf(w, w == 0.f ? 0.f : po[lane + 64 * i], o[i]);
-  }
-  const float inv = 1.f / L;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) out[lane + 64 * i] = from_f32<OutT>(o[i] * inv);
-  if (a.lse && lane == 0) a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = M * a.scale + logf(L);
 }
 
 // NR: query rows per KV head rounded up to 4, 8 or 16 (R = Tq * Hq/Hkv <= NR).
 // One launch does the whole decode attention: every wavefront writes its split's partials,
 // and the last wavefront of each (b, KV head) to arrive -- counted with a device-scope
 // atomic in the workspace -- merges them and resets the counter to zero for the next call.
-template <typename T, int D, int NR, typename OutT>
+// FUSED: one launch per decode step with the write cursor on the device (attn_decode_step):
+// c = *cursor; the new rows k_new/v_new [B, Tq, Hkv, D] are written to cache rows c .. c+Tq-1
+// and attended over as keys c .. c+Tq-1 straight from the sources (no wavefront of this launch
+// reads a cache row another one writes); the last (b, g) merge to finish sets *cursor = c+Tq
+// and kv_len_out[:] = c+Tq, after every wavefront has read the cursor.
+template <typename T, int D, int NR, typename OutT, bool FUSED>
 __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float* ws,
                                                     int n_splits) {
   typedef typename Mfma16<T>::vec vec;
@@ -117,8 +147,20 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
   float* ws_ml = ws_o + dec_o_floats(a.B, a.Hkv, D, n_splits);
 
   // a rejected batch element still takes part in the arrival count, with empty splits
-  const KeySet ks = key_set(a, b);
-  if (!ks.ok && lane == 0 && split == 0 && g == 0) report(a.err, dev_error_bit(a));
+  int cur = 0;  // fused step: the write position of this step
+  KeySet ks;
+  if constexpr (FUSED) {
+    cur = *a.cursor;
+    const bool fits = cur >= 0 && (int64_t)cur + a.Tq <= a.cap;
+    ks.base_row = (int64_t)b * a.cap;
+    ks.len = fits ? cur + a.Tq : 0;
+    ks.visit = ks.len;
+    ks.ok = fits;
+    if (!fits && lane == 0 && split == 0 && g == 0 && b == 0) report(a.err, SKV_DEV_CURSOR_FULL);
+  } else {
+    ks = key_set(a, b);
+    if (!ks.ok && lane == 0 && split == 0 && g == 0) report(a.err, dev_error_bit(a));
+  }
   // this split's share of the visited rows, in whole 16-key steps
   int per = (ks.visit + n_splits - 1) / n_splits;
   per = (per + 15) & ~15;
@@ -129,7 +171,7 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
   vec qa[DQ];
   {
     const int r = col;
-    if (r < R && ks.ok) {
+    if (r < R) {  // independent of kv_len, so these loads overlap the metadata load
       const int t = r / group, hh = r - t * group;
       const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + t) * a.Hq + g * group + hh) * D + 8 * quad;
 #pragma unroll
@@ -168,6 +210,24 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
   const int64_t rstride = (int64_t)a.Hkv * D;
   const T* kbase = (const T*)a.k + ks.base_row * rstride + (int64_t)g * D;
   const T* vbase = (const T*)a.v + ks.base_row * rstride + (int64_t)g * D;
+  // fused step: key j >= cur is new row j - cur of k_new/v_new (rows of batch element b)
+  const T* knew = nullptr;
+  const T* vnew = nullptr;
+  if constexpr (FUSED) {
+    knew = (const T*)a.k_new + (int64_t)b * a.Tq * rstride + (int64_t)g * D - (int64_t)cur * rstride;
+    vnew = (const T*)a.v_new + (int64_t)b * a.Tq * rstride + (int64_t)g * D - (int64_t)cur * rstride;
+    if (split == 0 && ks.ok) {  // this head's slice of the new rows goes into the cache
+      constexpr int VPR = D / 8;
+      for (int i = lane; i < a.Tq * VPR; i += 64) {
+        const int t = i / VPR, c8 = i - t * VPR;
+        const int64_t row = cur + t;
+        *(uint4*)((T*)a.k + ks.base_row * rstride + row * rstride + (int64_t)g * D + 8 * c8) =
+            *(const uint4*)(knew + row * rstride + 8 * c8);
+        *(uint4*)((T*)a.v + ks.base_row * rstride + row * rstride + (int64_t)g * D + 8 * c8) =
+            *(const uint4*)(vnew + row * rstride + 8 * c8);
+      }
+    }
+  }
   const float c2 = a.scale_log2;
   const int dc = col;    // PV phase: this lane's 8 output columns [8dc, 8dc+8)
   const int kg = quad;   // PV phase: keys kg, kg+4, ..., kg+60 of the tile
@@ -179,16 +239,18 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int j = tile + 16 * kb + col;
+      const T* kb_ptr = (FUSED && j >= cur) ? knew : kbase;
 #pragma unroll
       for (int c = 0; c < DQ; ++c)
-        kraw[kb][c] = j < end ? *(const uint4*)(kbase + (int64_t)j * rstride + 32 * c + 8 * quad)
+        kraw[kb][c] = j < end ? *(const uint4*)(kb_ptr + (int64_t)j * rstride + 32 * c + 8 * quad)
                               : make_uint4(0, 0, 0, 0);
     }
     uint4 vraw[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int j = tile + kg + 4 * i;
-      vraw[i] = (j < end && dc_ok) ? *(const uint4*)(vbase + (int64_t)j * rstride + 8 * dc)
+      const T* vb_ptr = (FUSED && j >= cur) ? vnew : vbase;
+      vraw[i] = (j < end && dc_ok) ? *(const uint4*)(vb_ptr + (int64_t)j * rstride + 8 * dc)
                                    : make_uint4(0, 0, 0, 0);
     }
     // S = Q K^T: s[kb][j] = score(row 4*quad+j, key tile+16kb+col)
@@ -293,21 +355,42 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
     }
   }
 
-  // arrive; the last split of this (b, g) merges
-  __threadfence();
+  // arrive; the last split of this (b, g) merges. Writers only release their partials
+  // (write-back); only the merging wavefront acquires (invalidate), so the L2 copy of the
+  // cache that other wavefronts are still reading is not dropped by every arrival.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   int last = 0;
   if (lane == 0) {
-    const int old = __hip_atomic_fetch_add(&counters[b * a.Hkv + g], 1, __ATOMIC_ACQ_REL,
+    const int old = __hip_atomic_fetch_add(&counters[b * a.Hkv + g], 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
     last = old == n_splits - 1;
   }
   last = __shfl(last, 0, 64);
   if (!last) return;
-  __threadfence();
-  for (int r = 0; r < R; ++r) merge_row<D, OutT>(a, group, ws_o, ws_ml, b, g, r, n_splits, lane);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  merge_rows<D, OutT>(a, group, ws_o, ws_ml, b, g, R, n_splits, lane);
   if (lane == 0)
     __hip_atomic_store(&counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (FUSED) {
+    // every wavefront of the launch read the cursor before it arrived: the last (b, g) merge
+    // may move it
+    int done = 0;
+    if (lane == 0) {
+      const int old = __hip_atomic_fetch_add(&counters[a.B * a.Hkv], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      done = old == a.B * a.Hkv - 1;
+    }
+    done = __shfl(done, 0, 64);
+    if (!done) return;
+    if (ks.ok) {
+      if (a.kv_len_out)
+        for (int bb = lane; bb < a.B; bb += 64) a.kv_len_out[bb] = cur + a.Tq;
+      if (lane == 0) *a.cursor = cur + a.Tq;
+    }
+    if (lane == 0)
+      __hip_atomic_store(&counters[a.B * a.Hkv], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Split count used by both the launcher and the workspace query.
@@ -324,18 +407,25 @@ size_t decode_workspace_bytes(int B, int Hkv, int D, int n_splits) {
           dec_ml_floats(B, Hkv, n_splits)) * sizeof(float);
 }
 
-template <typename T, int D, typename OutT>
-static hipError_t launch_decode_t(const AttnArgs& a, int group, float* ws, int n_splits,
+template <typename T, int D, typename OutT, bool FUSED>
+static hipError_t launch_decode_f(const AttnArgs& a, int group, float* ws, int n_splits,
                                   hipStream_t s) {
   const int R = a.Tq * group;
   dim3 grid(n_splits, a.Hkv, a.B), block(64);
   if (R <= 4)
-    hipLaunchKernelGGL((k_attn_decode<T, D, 4, OutT>), grid, block, 0, s, a, group, ws, n_splits);
+    hipLaunchKernelGGL((k_attn_decode<T, D, 4, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
   else if (R <= 8)
-    hipLaunchKernelGGL((k_attn_decode<T, D, 8, OutT>), grid, block, 0, s, a, group, ws, n_splits);
+    hipLaunchKernelGGL((k_attn_decode<T, D, 8, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
   else
-    hipLaunchKernelGGL((k_attn_decode<T, D, 16, OutT>), grid, block, 0, s, a, group, ws, n_splits);
+    hipLaunchKernelGGL((k_attn_decode<T, D, 16, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
   return hipGetLastError();
+}
+
+template <typename T, int D, typename OutT>
+static hipError_t launch_decode_t(const AttnArgs& a, int group, float* ws, int n_splits,
+                                  hipStream_t s) {
+  return a.cursor ? launch_decode_f<T, D, OutT, true>(a, group, ws, n_splits, s)
+                  : launch_decode_f<T, D, OutT, false>(a, group, ws, n_splits, s);
 }
 
 hipError_t launch_attn_decode(const AttnArgs& a, int dtype, int out_dtype, int D, void* ws,

@@ -60,6 +60,11 @@ struct AttnArgs {
   int full_cap;
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
+  // fused decode step only: new rows [B, Tq, Hkv, D], the shared write cursor, kv_len output
+  const void* k_new;
+  const void* v_new;
+  int32_t* cursor;
+  int32_t* kv_len_out;
 };
 
 __device__ __forceinline__ KeySet key_set(const AttnArgs& a, int b) {

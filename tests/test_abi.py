@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: the library loads and exports every function include/skv.h
+declares, the ctypes mirror of skv_attn_params has the C layout (offsets from gcc), and every
+host-checkable error returns its status before anything is launched (fake device pointers
+are never dereferenced on these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skv.h")
+
+skv = pytest.importorskip("streaming_kv_cache_write_amd")
+lib = skv.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_every_declared_function_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 15, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported by libskv.so"
+    assert set(names) == set(skv.EXPORTED)
+
+
+def test_params_struct_layout_matches_c(tmp_path):
+    fields = [f for f, _ in skv.skv_attn_params._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"skv.h\"\nint main(void){\n"
+                   + "".join(f'printf("%zu\\n", offsetof(skv_attn_params, {f}));\n' for f in fields)
+                   + 'printf("%zu\\n", sizeof(skv_attn_params));\nreturn 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    py = [getattr(skv.skv_attn_params, f).offset for f in fields] + [ctypes.sizeof(skv.skv_attn_params)]
+    assert out == py
+
+
+# fake, 16-byte aligned "device" addresses: validation fails before any of them is used
+P = 0x10000
+BAD = 0x10008  # 8-byte aligned only
+
+
+def params(**kw):
+    p = skv.skv_attn_params()
+    base = dict(B=1, Tq=8, Hq=4, Hkv=2, D=128, dtype=skv.SKV_BF16, out_dtype=skv.SKV_BF16, cap=64,
+                kv_len=32, mask=0, mask_block=1, scale=0.0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def attn(p, q=P, k=P, v=P, out=P):
+    return lib.attn_chunk_fwd(q, k, v, out, None, ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("kw,ptrs,status", [
+    ({}, dict(q=None), skv.SKV_ERR_NULL),
+    (dict(Hq=6, Hkv=4), {}, skv.SKV_ERR_SHAPE),
+    (dict(D=96), {}, skv.SKV_ERR_UNSUPPORTED),
+    (dict(dtype=7), {}, skv.SKV_ERR_DTYPE),
+    (dict(out_dtype=skv.SKV_F16), {}, skv.SKV_ERR_DTYPE),
+    (dict(kv_len=0), {}, skv.SKV_ERR_RANGE),       # fish-speech #1312: 0 is invalid
+    (dict(kv_len=65), {}, skv.SKV_ERR_RANGE),      # ... and so is capacity + 1
+    (dict(mask=1, kv_len=4), {}, skv.SKV_ERR_RANGE),  # causal chunk longer than the prefix
+    (dict(mask=2, mask_block=0), {}, skv.SKV_ERR_RANGE),
+    (dict(mask=5), {}, skv.SKV_ERR_RANGE),
+    (dict(flags=2), {}, skv.SKV_ERR_RANGE),
+    (dict(scale=-1.0), {}, skv.SKV_ERR_RANGE),
+    (dict(kv_len_dev=P, cu_seqlens_kv_dev=P), {}, skv.SKV_ERR_UNSUPPORTED),
+    (dict(cu_seqlens_kv_dev=P, flags=skv.FULL_CAPACITY_MASKED), {}, skv.SKV_ERR_UNSUPPORTED),
+    ({}, dict(k=BAD), skv.SKV_ERR_ALIGN),
+    (dict(Tq=1), {}, skv.SKV_ERR_NULL),            # decode-sized call without a workspace
+    (dict(Tq=1, workspace=P, workspace_bytes=16), {}, skv.SKV_ERR_RANGE),
+])
+def test_attention_host_errors(kw, ptrs, status):
+    assert attn(params(**kw), **ptrs) == status
+    assert lib.skv_last_error().decode()
+
+
+def test_valid_kv_len_bounds_pass_validation_of_workspace_query():
+    """1 and cap are valid (fish-speech #1312): the workspace query accepts them; decode-sized
+    calls need a workspace, chunk-sized ones do not."""
+    for kv_len in (1, 64):
+        assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=kv_len))) > 0
+    assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=8))) == 0
+    assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=0))) == 0
+    assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=65))) == 0
+    # the split-K workspace grows with the longest prefix it may see
+    small = lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=64, cap=64)))
+    large = lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=4096, cap=4096)))
+    assert large > small
+
+
+def test_write_host_errors():
+    f = lib.kv_write_indexed
+    # k_cache, v_cache, k_src, v_src, index, start, B, cap, n, Hkv, D, dtype, err, stream
+    assert f(None, None, P, None, None, 0, 1, 8, 1, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_NULL
+    assert f(P, P, P, None, None, 0, 1, 8, 1, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_NULL
+    assert f(P, None, P, None, None, 0, 1, 8, 1, 1, 64, 9, None, None) == skv.SKV_ERR_DTYPE
+    assert f(P, None, P, None, None, 0, 1, 8, 1, 1, 3, skv.SKV_BF16, None, None) == skv.SKV_ERR_ALIGN
+    assert f(BAD, None, P, None, None, 0, 1, 8, 1, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_ALIGN
+    assert f(P, None, P, None, None, 5, 1, 8, 4, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_RANGE
+    assert f(P, None, P, None, None, -1, 1, 8, 1, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_RANGE
+    # empty writes are valid no-ops that launch nothing
+    assert f(P, None, P, None, None, 0, 0, 8, 4, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_OK
+    assert f(P, None, P, None, None, 0, 1, 8, 0, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_OK
+
+
+def test_cursor_and_ring_host_errors():
+    assert lib.kv_cursor_advance(None, 1, 8, 1, P, None, None, None) == skv.SKV_ERR_NULL
+    assert lib.kv_cursor_advance(P, 0, 8, 1, P, None, None, None) == skv.SKV_ERR_SHAPE
+    assert lib.kv_ring_meta_bytes(3) == 48
+    h = ctypes.c_void_p()
+    # 0 <= sink < n_slots (flashdreams #763: the sink is part of the window, at least one
+    # rolling slot must remain)
+    for n_slots, sink in ((4, 4), (4, -1), (0, 0)):
+        st = lib.kv_ring_create(ctypes.byref(h), P, P, P, 2, 16, n_slots, sink, 1, 64, skv.SKV_BF16, None)
+        assert st == skv.SKV_ERR_RANGE and not h.value
+    st = lib.kv_ring_create(ctypes.byref(h), P, P, P, 2, 16, 4, 1, 1, 64, 11, None)
+    assert st == skv.SKV_ERR_DTYPE
+    assert lib.kv_ring_reserve(None, None, None) == skv.SKV_ERR_NULL
+    assert lib.kv_ring_write(None, P, P, None, None, None) == skv.SKV_ERR_NULL
+    assert lib.kv_ring_reset(None, None, None) == skv.SKV_ERR_NULL
+    assert lib.kv_ring_kv_len_dev(None) is None
+
+
+def test_decode_step_host_errors():
+    f = lib.attn_decode_step
+    p = params(Tq=1)
+    assert f(P, None, P, P, P, P, None, P, None, ctypes.byref(p), None) == skv.SKV_ERR_NULL
+    p = params(Tq=1, kv_len_dev=P)
+    assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(p), None) == skv.SKV_ERR_UNSUPPORTED
+    p = params(Tq=8)  # chunk-sized: not a decode step
+    assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(p), None) == skv.SKV_ERR_UNSUPPORTED
+    p = params(Tq=1, dtype=skv.SKV_F32, out_dtype=skv.SKV_F32)
+    assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(p), None) == skv.SKV_ERR_UNSUPPORTED
+    p = params(Tq=1)
+    assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(p), None) == skv.SKV_ERR_NULL  # workspace
