@@ -4,16 +4,16 @@
 // (fish-speech PR #1312 "perf(text2semantic): pass only active KV cache prefix to SDPA",
 // section Change); the step reads 2*kv_len*Hkv*D*elem bytes of K/V and does almost no math
 // per byte, so the kernel is built to stream K/V at HBM rate:
-//   * one wavefront per (split, KV head, batch element); the key range [0, visit) is cut into
+//   * one workgroup per (split, KV head, batch element); the key range [0, visit) is cut into
 //     gridDim.x equal parts computed on the device from kv_len, so a fixed grid (graph replay
-//     with a device kv_len) still spreads any length over every wavefront;
+//     with a device kv_len) still spreads any length over every workgroup;
 //   * all query rows of a GQA group (Hq/Hkv heads x Tq rows, <= 16) share each K/V load:
 //     S = Q K^T on v_mfma_f32_16x16x32 (K straight from global memory in the B-operand
 //     layout, the group's query rows as A), softmax in fp32, and P V on the vector ALUs with
 //     P kept in fp32 (each lane owns 8 output columns of a quarter of the keys);
-//   * every split writes its unnormalised (m, l, o) to the caller's workspace; the last split
-//     of each (b, KV head) to finish merges them with weights exp(m_s - max m), so one launch
-//     is the whole step (the workspace's arrival counters start at zero and are left at zero).
+//   * a workgroup of 4 wavefronts takes one split; its wavefronts merge in LDS. With several
+//     splits, each workgroup writes its unnormalised (m, l, o) to the caller's workspace and a
+//     second launch merges them with weights exp(m_s - max m).
 #include "common.h"
 
 namespace skv {
@@ -57,88 +57,148 @@ __device__ __forceinline__ void unpack8(const uint4& u, float* f) {
   for (int i = 0; i < 8; ++i) f[i] = to_f32(e[i]);
 }
 
-// Merge the n_splits partials of the R rows of (b, g) and write the output rows. Lane layout:
-// row r0 + lane/16 of each pass of 4 rows, columns [8*(lane%16), +8). One online pass over the
-// splits (running max M, weights exp2((m_s - M) * scale * log2 e)); the loads of 8 splits are
-// issued together and nothing in the loop branches on loaded data.
-template <int D, typename OutT>
-__device__ __forceinline__ void merge_rows(const AttnArgs& a, int group, const float* ws_o,
-                                           const float* ws_ml, int b, int g, int R, int n_splits,
-                                           int lane) {
-  constexpr int kBatch = 8;
-  const int dc = lane & 15;
-  const bool col_ok = dc < D / 8;
-  const float c2 = a.scale_log2;
-  for (int r0 = 0; r0 < R; r0 += 4) {
-    const int r = r0 + (lane >> 4);
-    const bool row_ok = r < R;
-    const size_t p0 = dec_part_index(b, g, row_ok ? r : 0, 0, a.Hkv, n_splits);
-    float M = -INFINITY, L = 0.f;
+constexpr int kDecWaves = 4;  // wavefronts per workgroup; they share one split's tiles
+// Per-lane merge state in the "row layout": row r0 + lane/16, columns [8*(lane%16), +8).
+struct MergeState {
+  float M, L, o[8];
+};
+
+__device__ __forceinline__ void merge_init(MergeState& st) {
+  st.M = -INFINITY;
+  st.L = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.o[e] = 0.f;
+}
+
+// Fold a partial (m, l, o) into st with weights exp2((m - M) * c2) (online, max-safe).
+__device__ __forceinline__ void merge_add(MergeState& st, float m, float l, const float* o,
+                                          float c2) {
+  const float m_new = fmaxf(st.M, m);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float wa = __builtin_amdgcn_exp2f((st.M - m_use) * c2);
+  const float wb = __builtin_amdgcn_exp2f((m - m_use) * c2);
+  st.L = st.L * wa + l * wb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.o[e] = st.o[e] * wa + o[e] * wb;
+  st.M = m_new;
+}
+
+// LDS staging of one state per (wavefront, row): m, l and D output columns.
+template <int D, int NR>
+struct DecStage {
+  float m[kDecWaves][NR];
+  float l[kDecWaves][NR];
+  float o[kDecWaves][NR][D];
+};
+
+// Combine the kDecWaves staged states of row r, columns [8dc, 8dc+8).
+template <int D, int NR>
+__device__ __forceinline__ void combine_staged(const DecStage<D, NR>& sg, int r, int dc,
+                                               float c2, MergeState& st) {
+  merge_init(st);
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) {
     float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.f;
-    for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
-      float2 ml[kBatch];
-      float4 oa[kBatch], ob[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int sp = s0 + u;
-        const bool ok = sp < n_splits;
-        ml[u] = ok ? *(const float2*)(ws_ml + 2 * (p0 + sp)) : make_float2(-INFINITY, 0.f);
-        const float* po = ws_o + (p0 + (ok ? sp : 0)) * D + 8 * dc;
-        oa[u] = (ok && col_ok) ? *(const float4*)po : make_float4(0.f, 0.f, 0.f, 0.f);
-        ob[u] = (ok && col_ok) ? *(const float4*)(po + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float m_new = fmaxf(M, ml[u].x);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float wa = __builtin_amdgcn_exp2f((M - m_use) * c2);       // rescale of the sum so far
-        const float wb = __builtin_amdgcn_exp2f((ml[u].x - m_use) * c2); // weight of split s
-        L = L * wa + ml[u].y * wb;
-        o[0] = o[0] * wa + oa[u].x * wb;
-        o[1] = o[1] * wa + oa[u].y * wb;
-        o[2] = o[2] * wa + oa[u].z * wb;
-        o[3] = o[3] * wa + oa[u].w * wb;
-        o[4] = o[4] * wa + ob[u].x * wb;
-        o[5] = o[5] * wa + ob[u].y * wb;
-        o[6] = o[6] * wa + ob[u].z * wb;
-        o[7] = o[7] * wa + ob[u].w * wb;
-        M = m_new;
-      }
-    }
-    if (!row_ok) continue;
-    const int t = r / group, h = g * group + (r - t * group);
-    OutT* out = (OutT*)a.out + (((int64_t)b * a.Tq + t) * a.Hq + h) * D + 8 * dc;
-    const float inv = L > 0.f ? 1.f / L : 0.f;  // L = 0: the batch element was rejected
-    if (col_ok) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = from_f32<OutT>(o[e] * inv);
-    }
-    if (a.lse && dc == 0)
-      a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = L > 0.f ? M * a.scale + logf(L) : -INFINITY;
+    for (int e = 0; e < 8; ++e) o[e] = dc < D / 8 ? sg.o[w][r][8 * dc + e] : 0.f;
+    merge_add(st, sg.m[w][r], sg.l[w][r], o, c2);
   }
 }
 
+template <typename OutT>
+__device__ __forceinline__ void write_row(const AttnArgs& a, int D, int group, int b, int g, int r,
+                                          int dc, const MergeState& st) {
+  const int t = r / group, h = g * group + (r - t * group);
+  const float inv = st.L > 0.f ? 1.f / st.L : 0.f;  // L = 0: the batch element was rejected
+  if (dc < D / 8) {
+    OutT* out = (OutT*)a.out + (((int64_t)b * a.Tq + t) * a.Hq + h) * D + 8 * dc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = from_f32<OutT>(st.o[e] * inv);
+  }
+  if (a.lse && dc == 0)
+    a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = st.L > 0.f ? st.M * a.scale + logf(st.L) : -INFINITY;
+}
+
+// The workgroup merges the n_splits partials of the R rows of (b, g) and writes the outputs:
+// wavefront w folds splits w, w + kDecWaves, ... (loads of 8 splits at a time, nothing
+// branching on loaded data), then wavefront 0 combines the kDecWaves states through LDS.
+template <int D, int NR, typename OutT>
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, const float* ws_o,
+                                             const float* ws_ml, DecStage<D, NR>& sg, int b, int g,
+                                             int n_splits) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int dc = lane & 15;
+  const bool dc_ok = dc < D / 8;
+  const int R = a.Tq * group;
+  const float c2 = a.scale_log2;
+    for (int r0 = 0; r0 < NR; r0 += 4) {
+      const int r = r0 + (lane >> 4);
+      const bool row_ok = r < R;
+      const size_t p0 = dec_part_index(b, g, row_ok ? r : 0, 0, a.Hkv, n_splits);
+      MergeState st;
+      merge_init(st);
+      constexpr int kBatch = 8;
+      for (int s0 = wave; s0 < n_splits; s0 += kBatch * kDecWaves) {
+        float2 ml[kBatch];
+        float4 oa[kBatch], ob[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int sp = s0 + u * kDecWaves;
+          const bool ok = sp < n_splits;
+          ml[u] = ok ? *(const float2*)(ws_ml + 2 * (p0 + sp)) : make_float2(-INFINITY, 0.f);
+          const float* po = ws_o + (p0 + (ok ? sp : 0)) * D + 8 * dc;
+          oa[u] = (ok && dc_ok) ? *(const float4*)po : make_float4(0.f, 0.f, 0.f, 0.f);
+          ob[u] = (ok && dc_ok) ? *(const float4*)(po + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float o8[8] = {oa[u].x, oa[u].y, oa[u].z, oa[u].w, ob[u].x, ob[u].y, ob[u].z, ob[u].w};
+          merge_add(st, ml[u].x, ml[u].y, o8, c2);
+        }
+      }
+      __syncthreads();  // the previous pass's reads of the staging area are done
+      if (row_ok) {
+        if (dc == 0) {
+          sg.m[wave][r] = st.M;
+          sg.l[wave][r] = st.L;
+        }
+        if (dc_ok)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sg.o[wave][r][8 * dc + e] = st.o[e];
+      }
+      __syncthreads();
+      if (wave == 0 && row_ok) {
+        MergeState fin;
+        combine_staged<D, NR>(sg, r, dc, c2, fin);
+        write_row<OutT>(a, D, group, b, g, r, dc, fin);
+      }
+    }
+}
+
 // NR: query rows per KV head rounded up to 4, 8 or 16 (R = Tq * Hq/Hkv <= NR).
-// One launch does the whole decode attention: every wavefront writes its split's partials,
-// and the last wavefront of each (b, KV head) to arrive -- counted with a device-scope
-// atomic in the workspace -- merges them and resets the counter to zero for the next call.
+// Workgroup = kDecWaves wavefronts per (split, KV head g, batch element b); the split's key
+// range is cut into 64-key tiles dealt round-robin to the wavefronts. Each wavefront keeps its
+// own online-softmax state; the workgroup merges them in LDS. With one split that is the
+// output; otherwise the workgroup's partial goes to the workspace and k_decode_merge, a second
+// launch, merges the splits. (Merging in this launch, by the last workgroup to arrive, needs a
+// release fence per workgroup -- an L2 write-back on this multi-XCD chip -- and measured slower
+// than the second launch at every length tried, 64 to 32768 keys.)
 // FUSED: one launch per decode step with the write cursor on the device (attn_decode_step):
 // c = *cursor; the new rows k_new/v_new [B, Tq, Hkv, D] are written to cache rows c .. c+Tq-1
 // and attended over as keys c .. c+Tq-1 straight from the sources (no wavefront of this launch
-// reads a cache row another one writes); the last (b, g) merge to finish sets *cursor = c+Tq
-// and kv_len_out[:] = c+Tq, after every wavefront has read the cursor.
+// reads a cache row another one writes); the last (b, g) to finish sets *cursor = c+Tq and
+// kv_len_out[:] = c+Tq, after every wavefront has read the cursor.
 template <typename T, int D, int NR, typename OutT, bool FUSED>
-__global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float* ws,
-                                                    int n_splits) {
+__global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int group, float* ws,
+                                                                int n_splits) {
   typedef typename Mfma16<T>::vec vec;
   constexpr int DQ = D / 32;  // 32-wide d chunks of the QK^T contraction
-  __shared__ __attribute__((aligned(16))) float P[kDecBN][kDecRows];
-  __shared__ float alpha_s[kDecRows];
+  __shared__ __attribute__((aligned(16))) float P[kDecWaves][kDecBN][kDecRows];
+  __shared__ float alpha_s[kDecWaves][kDecRows];
+  __shared__ __attribute__((aligned(16))) DecStage<D, NR> sg;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int R = a.Tq * group;
   // workspace: arrival counters first (a fixed place for any split count), then partials
@@ -156,14 +216,14 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
     ks.len = fits ? cur + a.Tq : 0;
     ks.visit = ks.len;
     ks.ok = fits;
-    if (!fits && lane == 0 && split == 0 && g == 0 && b == 0) report(a.err, SKV_DEV_CURSOR_FULL);
+    if (!fits && threadIdx.x == 0 && split == 0 && g == 0 && b == 0) report(a.err, SKV_DEV_CURSOR_FULL);
   } else {
     ks = key_set(a, b);
-    if (!ks.ok && lane == 0 && split == 0 && g == 0) report(a.err, dev_error_bit(a));
+    if (!ks.ok && threadIdx.x == 0 && split == 0 && g == 0) report(a.err, dev_error_bit(a));
   }
-  // this split's share of the visited rows, in whole 16-key steps
+  // this split's share of the visited rows, in whole 64-key tiles
   int per = (ks.visit + n_splits - 1) / n_splits;
-  per = (per + 15) & ~15;
+  per = (per + kDecBN - 1) & ~(kDecBN - 1);
   const int start = split * per;
   const int end = ks.ok ? min(ks.visit, start + per) : 0;
 
@@ -216,7 +276,7 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
   if constexpr (FUSED) {
     knew = (const T*)a.k_new + (int64_t)b * a.Tq * rstride + (int64_t)g * D - (int64_t)cur * rstride;
     vnew = (const T*)a.v_new + (int64_t)b * a.Tq * rstride + (int64_t)g * D - (int64_t)cur * rstride;
-    if (split == 0 && ks.ok) {  // this head's slice of the new rows goes into the cache
+    if (split == 0 && wave == 0 && ks.ok) {  // this head's slice of the new rows goes into the cache
       constexpr int VPR = D / 8;
       for (int i = lane; i < a.Tq * VPR; i += 64) {
         const int t = i / VPR, c8 = i - t * VPR;
@@ -232,8 +292,11 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
   const int dc = col;    // PV phase: this lane's 8 output columns [8dc, 8dc+8)
   const int kg = quad;   // PV phase: keys kg, kg+4, ..., kg+60 of the tile
   const bool dc_ok = dc < D / 8;  // D = 64 leaves half of the lanes without columns
+  float (*Pw)[kDecRows] = P[wave];
 
-  for (int tile = start; tile < end; tile += kDecBN) {
+  // the wavefronts of the workgroup take the split's tiles in turn; no workgroup barrier in
+  // here (trip counts differ): P and alpha_s are per wavefront
+  for (int tile = start + kDecBN * wave; tile < end; tile += kDecBN * kDecWaves) {
     // issue every K and V load of the tile first
     uint4 kraw[4][DQ];
 #pragma unroll
@@ -294,14 +357,16 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      *(float4*)&P[16 * kb + col][4 * quad] = make_float4(s[kb][0], s[kb][1], s[kb][2], s[kb][3]);
+      *(float4*)&Pw[16 * kb + col][4 * quad] = make_float4(s[kb][0], s[kb][1], s[kb][2], s[kb][3]);
     if (col == 0)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) alpha_s[4 * quad + j] = alpha[j];
-    __syncthreads();
+      for (int j = 0; j < 4; ++j) alpha_s[wave][4 * quad + j] = alpha[j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const float al = alpha_s[r];
+      const float al = alpha_s[wave][r];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[r][e] *= al;
     }
@@ -309,7 +374,7 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
     for (int i = 0; i < 16; ++i) {
       float v[8];
       unpack8<T>(vraw[i], v);
-      const float* pr = P[kg + 4 * i];
+      const float* pr = Pw[kg + 4 * i];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const float p = pr[r];
@@ -317,7 +382,10 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
         for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, v[e], acc[r][e]);
       }
     }
-    __syncthreads();  // P and alpha_s are rewritten by the next tile
+    // P and alpha_s are rewritten by the next tile of this wavefront
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   // row sums: each of the 16 lanes of a quad holds part of rows 4*quad+j
@@ -333,72 +401,97 @@ __global__ void __launch_bounds__(64) k_attn_decode(AttnArgs a, int group, float
       acc[r][e] += __shfl_xor(acc[r][e], 16, 64);
       acc[r][e] += __shfl_xor(acc[r][e], 32, 64);
     }
-  if (kg == 0 && dc_ok) {
+  // stage this wavefront's state, then merge the workgroup's wavefronts row by row
+  if (col == 0)
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (r < R) {
-        float* po = ws_o + dec_part_index(b, g, r, split, a.Hkv, n_splits) * D + 8 * dc;
-        *(float4*)po = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-        *(float4*)(po + 4) = make_float4(acc[r][4], acc[r][5], acc[r][6], acc[r][7]);
+    for (int j = 0; j < 4; ++j)
+      if (4 * quad + j < NR) {
+        sg.m[wave][4 * quad + j] = m[j];
+        sg.l[wave][4 * quad + j] = l[j];
       }
-    }
-  }
-  if (col == 0) {
+  if (kg == 0 && dc_ok)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * quad + j;
-      if (r < R) {
-        const size_t pi = dec_part_index(b, g, r, split, a.Hkv, n_splits);
-        ws_ml[2 * pi] = m[j];
-        ws_ml[2 * pi + 1] = l[j];
-      }
-    }
-  }
-
-  // arrive; the last split of this (b, g) merges. Writers only release their partials
-  // (write-back); only the merging wavefront acquires (invalidate), so the L2 copy of the
-  // cache that other wavefronts are still reading is not dropped by every arrival.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sg.o[wave][r][8 * dc + e] = acc[r][e];
   __syncthreads();
-  int last = 0;
-  if (lane == 0) {
-    const int old = __hip_atomic_fetch_add(&counters[b * a.Hkv + g], 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    last = old == n_splits - 1;
+
+  if (n_splits == 1) {  // the workgroup saw every key: its merge is the output
+    if (wave == 0)
+      for (int r0 = 0; r0 < R; r0 += 4) {
+        const int r = r0 + (lane >> 4);
+        MergeState st;
+        if (r < R) {
+          combine_staged<D, NR>(sg, r, dc, c2, st);
+          write_row<OutT>(a, D, group, b, g, r, dc, st);
+        }
+      }
+  } else {
+    // the workgroup's partial goes to the workspace
+    if (wave == 0)
+      for (int r0 = 0; r0 < R; r0 += 4) {
+        const int r = r0 + (lane >> 4);
+        if (r >= R) continue;
+        MergeState st;
+        combine_staged<D, NR>(sg, r, dc, c2, st);
+        const size_t pi = dec_part_index(b, g, r, split, a.Hkv, n_splits);
+        if (dc_ok) {
+          float* po = ws_o + pi * D + 8 * dc;
+          *(float4*)po = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
+          *(float4*)(po + 4) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
+        }
+        if (dc == 0) *(float2*)(ws_ml + 2 * pi) = make_float2(st.M, st.L);
+      }
+    return;  // k_decode_merge finishes the step
   }
-  last = __shfl(last, 0, 64);
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  merge_rows<D, OutT>(a, group, ws_o, ws_ml, b, g, R, n_splits, lane);
-  if (lane == 0)
-    __hip_atomic_store(&counters[b * a.Hkv + g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (FUSED) {
-    // every wavefront of the launch read the cursor before it arrived: the last (b, g) merge
-    // may move it
-    int done = 0;
-    if (lane == 0) {
+    // one split per (b, g): every workgroup of the launch read the cursor before it got here,
+    // so the last one to finish may move it (an arrival count only; no data is handed over)
+    if (threadIdx.x == 0) {
       const int old = __hip_atomic_fetch_add(&counters[a.B * a.Hkv], 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
-      done = old == a.B * a.Hkv - 1;
+      if (old == a.B * a.Hkv - 1) {
+        if (ks.ok) {
+          if (a.kv_len_out)
+            for (int bb = 0; bb < a.B; ++bb) a.kv_len_out[bb] = cur + a.Tq;
+          *a.cursor = cur + a.Tq;
+        }
+        __hip_atomic_store(&counters[a.B * a.Hkv], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    done = __shfl(done, 0, 64);
-    if (!done) return;
-    if (ks.ok) {
-      if (a.kv_len_out)
-        for (int bb = lane; bb < a.B; bb += 64) a.kv_len_out[bb] = cur + a.Tq;
-      if (lane == 0) *a.cursor = cur + a.Tq;
+  }
+}
+
+// Second launch of the two-kernel variant: one workgroup per (b, KV head) merges the splits.
+// In the fused step, workgroup (0, 0) also moves the cursor: every workgroup of the first
+// launch read it before this launch started, and no workgroup of this one reads it otherwise.
+template <int D, int NR, typename OutT, bool FUSED>
+__global__ void __launch_bounds__(64 * kDecWaves) k_decode_merge(AttnArgs a, int group, float* ws,
+                                                                 int n_splits) {
+  __shared__ __attribute__((aligned(16))) DecStage<D, NR> sg;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const float* ws_o = ws + dec_counter_floats(a.B, a.Hkv);
+  const float* ws_ml = ws_o + dec_o_floats(a.B, a.Hkv, D, n_splits);
+  merge_splits<D, NR, OutT>(a, group, ws_o, ws_ml, sg, b, g, n_splits);
+  if constexpr (FUSED) {
+    if (b == 0 && g == 0 && threadIdx.x == 0) {
+      const int cur = *a.cursor;
+      if (cur >= 0 && (int64_t)cur + a.Tq <= a.cap) {
+        if (a.kv_len_out)
+          for (int bb = 0; bb < a.B; ++bb) a.kv_len_out[bb] = cur + a.Tq;
+        *a.cursor = cur + a.Tq;
+      }
     }
-    if (lane == 0)
-      __hip_atomic_store(&counters[a.B * a.Hkv], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // Split count used by both the launcher and the workspace query.
 int decode_splits(int B, int Hkv, int max_len) {
   const int tiles = (max_len + kDecBN - 1) / kDecBN;
-  int target = 2048 / (B * Hkv);  // about two wavefronts per SIMD over the whole chip
+  const int by_tiles = (tiles + kDecWaves - 1) / kDecWaves;  // one tile per wavefront at most
+  int target = 2048 / (B * Hkv * kDecWaves);  // about two wavefronts per SIMD over the chip
   if (target < 1) target = 1;
-  int s = tiles < target ? tiles : target;
+  int s = by_tiles < target ? by_tiles : target;
   return s < 1 ? 1 : s;
 }
 
@@ -407,18 +500,25 @@ size_t decode_workspace_bytes(int B, int Hkv, int D, int n_splits) {
           dec_ml_floats(B, Hkv, n_splits)) * sizeof(float);
 }
 
+template <typename T, int D, int NR, typename OutT, bool FUSED>
+static hipError_t launch_decode_nr(const AttnArgs& a, int group, float* ws, int n_splits,
+                                   hipStream_t s) {
+  dim3 grid(n_splits, a.Hkv, a.B), block(64 * kDecWaves);
+  hipLaunchKernelGGL((k_attn_decode<T, D, NR, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_splits == 1) return e;
+  hipLaunchKernelGGL((k_decode_merge<D, NR, OutT, FUSED>), dim3(a.Hkv, a.B), block, 0, s, a, group, ws,
+                     n_splits);
+  return hipGetLastError();
+}
+
 template <typename T, int D, typename OutT, bool FUSED>
 static hipError_t launch_decode_f(const AttnArgs& a, int group, float* ws, int n_splits,
                                   hipStream_t s) {
   const int R = a.Tq * group;
-  dim3 grid(n_splits, a.Hkv, a.B), block(64);
-  if (R <= 4)
-    hipLaunchKernelGGL((k_attn_decode<T, D, 4, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
-  else if (R <= 8)
-    hipLaunchKernelGGL((k_attn_decode<T, D, 8, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
-  else
-    hipLaunchKernelGGL((k_attn_decode<T, D, 16, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
-  return hipGetLastError();
+  if (R <= 4) return launch_decode_nr<T, D, 4, OutT, FUSED>(a, group, ws, n_splits, s);
+  if (R <= 8) return launch_decode_nr<T, D, 8, OutT, FUSED>(a, group, ws, n_splits, s);
+  return launch_decode_nr<T, D, 16, OutT, FUSED>(a, group, ws, n_splits, s);
 }
 
 template <typename T, int D, typename OutT>
