@@ -78,8 +78,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   constexpr int DB = D / 32;           // 32-row d blocks of O^T
   constexpr int VPR = D / 8;           // 16-byte vectors per K/V row
   constexpr int LOADS = BN * VPR / 256;
-  __shared__ __attribute__((aligned(16))) T Ks[BN * LDK];
-  __shared__ __attribute__((aligned(16))) TV Vs[BN * LDK];
+  __shared__ __attribute__((aligned(16))) T Ks[2][BN * LDK];  // double-buffered tiles
+  __shared__ __attribute__((aligned(16))) TV Vs[2][BN * LDK];
 
   // workgroup -> (query tile, head, batch element); tiles of one head stay on one XCD
   const int nb = gridDim.x, bid = blockIdx.x;
@@ -147,21 +147,21 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int idx = tid + 256 * i;
       const int key = idx / VPR, c8 = idx % VPR;
-      *(uint4*)&Ks[key * LDK + 8 * c8] = kr[i];
+      *(uint4*)&Ks[buf][key * LDK + 8 * c8] = kr[i];
       if constexpr (PV16 && !std::is_same<T, f16_t>::value) {
         const T* e = (const T*)&vr[i];
         typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 h8;
         h8 hv;
 #pragma unroll
         for (int k = 0; k < 8; ++k) hv[k] = (f16_t)(float)e[k];
-        *(h8*)&Vs[key * LDK + 8 * c8] = hv;
+        *(h8*)&Vs[buf][key * LDK + 8 * c8] = hv;
       } else {
-        *(uint4*)&Vs[key * LDK + 8 * c8] = vr[i];
+        *(uint4*)&Vs[buf][key * LDK + 8 * c8] = vr[i];
       }
     }
   };
@@ -172,15 +172,15 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   float m = -INFINITY, lsum = 0.f;
   const float c = a.scale_log2;
 
-  // One 64-key tile: stage it, S^T = K Q^T, online softmax, O^T += V^T P^T.
+  // One 64-key tile held in LDS buffer `buf`: S^T = K Q^T, online softmax, O^T += V^T P^T;
+  // meanwhile the next tile (already in registers) goes to the other buffer and the one after
+  // it is fetched from HBM -- one workgroup barrier per tile.
   // MASKED selects the variant with the per-score visibility test; the two variants run in
   // separate loops so no branch sits between the S^T products and their use.
-  auto step = [&](int tile, auto masked) {
+  auto step = [&](int tile, int buf, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
-    __syncthreads();  // the previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    if (tile + BN < key_end) load_tile(tile + BN);
+    const T* Kt = Ks[buf];
+    const TV* Vt = Vs[buf];
 
     // s[sb][4i+j] = score(key tile+32sb+8i+4hi+j, query my_q)
     f32x16 s[2];
@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
       s[sb] = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < DC; ++cc) {
-        const vec ka = *(const vec*)&Ks[(sb * 32 + l32) * LDK + 16 * cc + 8 * hi];
+        const vec ka = *(const vec*)&Kt[(sb * 32 + l32) * LDK + 16 * cc + 8 * hi];
         s[sb] = Mfma<T>::mma(ka, qreg[cc], s[sb]);
       }
     }
@@ -222,8 +222,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
       }
     lsum = lsum * alpha + psum;
     m = m_new;
+    // rescale O only when some row's max moved in this wavefront (alpha == 1 exactly otherwise)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
 
     // P^T as B operands, one per 16-key chunk: k slot jj of lane half hi holds
     // key 4hi+jj (jj < 4) or 8+4hi+(jj-4) (jj >= 4) of the chunk
@@ -242,17 +245,27 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const int key = 16 * kc + (jj < 4 ? 4 * hi + jj : 8 + 4 * hi + (jj - 4));
-          va[jj] = Vs[key * LDK + 32 * db + l32];
+          va[jj] = Vt[key * LDK + 32 * db + l32];
         }
         o[db] = Mfma<TV>::mma(va, pb[kc], o[db]);
       }
     }
+    if (tile + BN < key_end) {
+      store_tile(buf ^ 1);  // nobody reads that buffer: every wave passed the last barrier
+      if (tile + 2 * BN < key_end) load_tile(tile + 2 * BN);
+    }
+    __syncthreads();
   };
 
-  if (key_end > 0) load_tile(0);
-  int tile = 0;
-  for (; tile < full_end; tile += BN) step(tile, std::false_type{});
-  for (; tile < key_end; tile += BN) step(tile, std::true_type{});
+  if (key_end > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (BN < key_end) load_tile(BN);
+    __syncthreads();
+  }
+  int tile = 0, buf = 0;
+  for (; tile < full_end; tile += BN, buf ^= 1) step(tile, buf, std::false_type{});
+  for (; tile < key_end; tile += BN, buf ^= 1) step(tile, buf, std::true_type{});
 
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
