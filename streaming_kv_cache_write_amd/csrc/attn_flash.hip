@@ -44,6 +44,13 @@ template <> struct Mfma<f16_t> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle, range checked
+// against num_records: out-of-range loads return zero).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <typename OutT> __device__ __forceinline__ void store4(OutT* p, float a, float b, float c,
                                                                 float d);
 template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c,
@@ -73,13 +80,15 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   typedef typename std::conditional<PV16, f16_t, T>::type TV;  // type of V and P in P V
   typedef typename Mfma<TV>::vec vecv;
   constexpr int BN = kFlashBN;
-  constexpr int LDK = D + 8;           // LDS row stride in elements (16-byte pad)
+  constexpr int LDK = D + 8;           // K row stride in LDS, elements (16-byte pad)
+  constexpr int LDV = D + 16;          // V row stride: 32-byte pad, so the transposed read of
+                                       // 4 rows x 32 bytes by 16 lanes hits 32 distinct banks
   constexpr int DC = D / 16;           // 16-wide d chunks of the QK^T contraction
   constexpr int DB = D / 32;           // 32-row d blocks of O^T
   constexpr int VPR = D / 8;           // 16-byte vectors per K/V row
   constexpr int LOADS = BN * VPR / 256;
   __shared__ __attribute__((aligned(16))) T Ks[2][BN * LDK];  // double-buffered tiles
-  __shared__ __attribute__((aligned(16))) TV Vs[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) TV Vs[2][BN * LDV];
 
   // workgroup -> (query tile, head, batch element); tiles of one head stay on one XCD
   const int nb = gridDim.x, bid = blockIdx.x;
@@ -132,19 +141,29 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   const T* vbase = (const T*)a.v + ks.base_row * rstride + (int64_t)g * D;
 
   uint4 kr[LOADS], vr[LOADS];
+  // Tile loads are buffer loads: a per-tile resource (uniform base = the tile's first row,
+  // size = its rows that exist) plus a loop-invariant 32-bit lane offset. Rows past the end of
+  // the visited range fall outside the resource and read as zero, so no load is branched,
+  // predicated or followed by a zero fill, and no per-load address arithmetic is needed.
+  uint32_t ld_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int idx = tid + 256 * i;
+    ld_off[i] = (uint32_t)(((idx / VPR) * rstride + 8 * (idx % VPR)) * sizeof(T));
+  }
+  const int row_bytes = (int)(rstride * sizeof(T));
   auto load_tile = [&](int tile) {
+    const int rows = min(ks.visit - tile, BN);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (int64_t)tile * rstride), (short)0, rows * row_bytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (int64_t)tile * rstride), (short)0, rows * row_bytes, kBufferRsrcWord3);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int idx = tid + 256 * i;
-      const int key = idx / VPR, c8 = idx % VPR;
-      const int j = tile + key;
-      if (j < ks.visit) {
-        kr[i] = *(const uint4*)(kbase + (int64_t)j * rstride + 8 * c8);
-        vr[i] = *(const uint4*)(vbase + (int64_t)j * rstride + 8 * c8);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);  // rows past the buffer read as zero, never as data
-        vr[i] = make_uint4(0, 0, 0, 0);
-      }
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)ld_off[i], 0, 0);
+      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)ld_off[i], 0, 0);
+      __builtin_memcpy(&kr[i], &a, 16);
+      __builtin_memcpy(&vr[i], &c, 16);
     }
   };
   auto store_tile = [&](int buf) {
@@ -159,12 +178,16 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
         h8 hv;
 #pragma unroll
         for (int k = 0; k < 8; ++k) hv[k] = (f16_t)(float)e[k];
-        *(h8*)&Vs[buf][key * LDK + 8 * c8] = hv;
+        *(h8*)&Vs[buf][key * LDV + 8 * c8] = hv;
       } else {
-        *(uint4*)&Vs[buf][key * LDK + 8 * c8] = vr[i];
+        *(uint4*)&Vs[buf][key * LDV + 8 * c8] = vr[i];
       }
     }
   };
+
+  // transposed V reads: row and column offsets of this lane's 8-byte chunk (see the PV step)
+  const int tr_row = (lane & 15) >> 2;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 o[DB];
 #pragma unroll
@@ -241,12 +264,16 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
+        // A operand V^T (32 d rows x 16 keys) by two transposed LDS reads: lane k of each
+        // 16-lane group points at V[key0 + k/4][d0 + 4(k%4)], and lane i receives
+        // V[key0 + t][d0 + i], t = 0..3 -- four keys of one d column. The keys are the MFMA
+        // k slots 0..3 (keys 4hi+t of the chunk) and 4..7 (keys 8+4hi+t), the order P holds.
+        const TV* vp = Vt + (16 * kc + 4 * hi + tr_row) * LDV + 32 * db + tr_col;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * LDV));
         vecv va;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int key = 16 * kc + (jj < 4 ? 4 * hi + jj : 8 + 4 * hi + (jj - 4));
-          va[jj] = Vt[key * LDK + 32 * db + l32];
-        }
+        __builtin_memcpy(&va, &x0, 8);
+        __builtin_memcpy((char*)&va + 8, &x1, 8);
         o[db] = Mfma<TV>::mma(va, pb[kc], o[db]);
       }
     }
