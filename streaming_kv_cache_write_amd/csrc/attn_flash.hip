@@ -14,12 +14,18 @@
 //     of the 32 keys, so the row max / row sum need only in-lane work plus one exchange with
 //     lane^32.
 //   * Online softmax in fp32 with exp2 and the scale folded into one FMA per score; masked
-//     entries are selected to -inf (never multiplied), so a masked key contributes exactly 0
-//     and a tile that leaves the running max unchanged rescales by exactly 1.
+//     entries are selected to -inf (never multiplied), so a masked key contributes exactly 0.
+//     The reference max moves (and O is rescaled) only when a tile's max passes it by more than
+//     2^8 in probability; otherwise the rescale factor is exactly 1 and skipped. Row sums add
+//     the rounded probabilities with dot2 instructions.
 //   * O^T += V^T P^T with the same MFMA: P stays in registers (the accumulator's key order is
 //     mapped onto the MFMA's k slots, and V^T is read from LDS in that same order).
-//   * K/V tiles of 64 keys are staged in LDS (rows padded by 16 bytes against bank conflicts);
-//     the next tile's global loads are issued before the current tile's math.
+//   * K/V tiles of 64 keys are staged in LDS (K rows padded by 16 bytes, V rows by 64 bytes,
+//     so neither the K reads nor the transposed V reads conflict on the 64 banks); the next
+//     tile's global loads are issued before the current tile's math.
+//   * The two wavefronts sharing a SIMD (one from each of the CU's two workgroups) overlap
+//     matrix-core and vector work: a wavefront raises its priority while it issues MFMAs, so
+//     the other one's softmax fills the vector ALU meanwhile.
 //   * Workgroup ids are remapped so the query tiles of one (b, h) run on the same XCD and
 //     share its L2 copy of K/V (dispatch hands consecutive workgroup ids to the 8 XCDs in turn).
 #include <type_traits>
@@ -43,6 +49,32 @@ template <> struct Mfma<f16_t> {
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The running max used as the softmax reference moves only when a tile's max exceeds it by more
+// than this many powers of two (after the log2(e) * scale fold). Until then the stale reference
+// is kept: probabilities stay below 2^8, far inside bf16/fp16 range, O needs no rescale, and the
+// final O / l and lse are unchanged because numerator and denominator share the reference.
+constexpr float kRescaleLog2 = 8.f;
+
+// s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt fields left at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// row sum of 8 probabilities as rounded for the P V product, by 4 dot2 with (1, 1)
+__device__ __forceinline__ float sum8(bf16x8 p, float acc) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf2;
+  const bf2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf2{p[2 * i], p[2 * i + 1]}, one, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float sum8(f16x8 p, float acc) {
+  typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2;
+  const h2 one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(h2{p[2 * i], p[2 * i + 1]}, one, acc, false);
+  return acc;
+}
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
@@ -81,8 +113,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   typedef typename Mfma<TV>::vec vecv;
   constexpr int BN = kFlashBN;
   constexpr int LDK = D + 8;           // K row stride in LDS, elements (16-byte pad)
-  constexpr int LDV = D + 16;          // V row stride: 32-byte pad, so the transposed read of
-                                       // 4 rows x 32 bytes by 16 lanes hits 32 distinct banks
+  constexpr int LDV = D + 32;          // V row stride: 64-byte pad. A row is then 16 dwords
+                                       // (mod 64) on from the last, and the transposed read of
+                                       // two 16-lane groups (4 rows x 2 x 32 bytes) hits 64
+                                       // distinct banks
   constexpr int DC = D / 16;           // 16-wide d chunks of the QK^T contraction
   constexpr int DB = D / 32;           // 32-row d blocks of O^T
   constexpr int VPR = D / 8;           // 16-byte vectors per K/V row
@@ -124,6 +158,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
       if (q_ok) qreg[c] = *(const vec*)(qp + 16 * c);
       else qreg[c] = vec{};
     }
+    // Wait for these loads here, on every path. Otherwise the compiler may still count them as
+    // outstanding at the head of the tile loop and wait there for all loads -- including the
+    // next tile's, issued one step earlier to hide their latency.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
   // key range: the workgroup's last query bounds it; keys below key_full are visible to
@@ -207,6 +245,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
 
     // s[sb][4i+j] = score(key tile+32sb+8i+4hi+j, query my_q)
     f32x16 s[2];
+    __builtin_amdgcn_s_setprio(1);  // matrix-core phase: issue ahead of softmax waves
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       s[sb] = f32x16{};
@@ -216,6 +255,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
         s[sb] = Mfma<T>::mma(ka, qreg[cc], s[sb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     float sv[2][16];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -230,36 +270,36 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[sb][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m, mt);
+    // (mt - m) is NaN when both are -inf (a row with nothing visible yet): no move
+    const bool grow = (mt - m) * c > kRescaleLog2;
+    const float m_new = grow ? mt : m;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2((m - m_use) * c);  // exactly 1 when the max is unchanged
+    const float alpha = fast_exp2((m - m_use) * c);  // exactly 1 while the reference stays
     const float mc = m_use * c;
-    float psum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sv[sb][r], c, -mc));
-        sv[sb][r] = p;
-        psum += p;
-      }
-    lsum = lsum * alpha + psum;
+      for (int r = 0; r < 16; ++r) sv[sb][r] = fast_exp2(fmaf(sv[sb][r], c, -mc));
     m = m_new;
-    // rescale O only when some row's max moved in this wavefront (alpha == 1 exactly otherwise)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+    if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
 
     // P^T as B operands, one per 16-key chunk: k slot jj of lane half hi holds
-    // key 4hi+jj (jj < 4) or 8+4hi+(jj-4) (jj >= 4) of the chunk
+    // key 4hi+jj (jj < 4) or 8+4hi+(jj-4) (jj >= 4) of the chunk. The row sum adds the
+    // rounded values, the weights the product actually applies.
     vecv pb[4];
+    float psum = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int sb = kc >> 1, r0 = 8 * (kc & 1);
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) pb[kc][jj] = (TV)sv[sb][r0 + jj];
+      psum = sum8(pb[kc], psum);
     }
+    lsum = lsum * alpha + psum;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
@@ -277,6 +317,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
         o[db] = Mfma<TV>::mma(va, pb[kc], o[db]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (tile + BN < key_end) {
       store_tile(buf ^ 1);  // nobody reads that buffer: every wave passed the last barrier
       if (tile + 2 * BN < key_end) load_tile(tile + 2 * BN);
