@@ -167,7 +167,7 @@ skv_status kv_ring_destroy(skv_ring* ring);
  * Tq <= 4 (decode-sized chunks) in bf16/f16 uses a split-K path that needs a workspace of
  * attn_workspace_bytes(params) bytes (caller device memory, 16-byte aligned); other shapes
  * need none. The workspace must be zero-filled once before its first use: its first bytes
- * hold arrival counters (B*Hkv int32, at offset 0 whatever the split count) that every call
+ * hold arrival counters (B*Hkv + 1 int32, at offset 0 whatever the split count) that every call
  * leaves at zero again, so one zero-filled workspace of the largest size needed can serve
  * every later call. Calls sharing one workspace must not overlap in time (they are ordered
  * when issued on one stream).

@@ -1,64 +1,137 @@
-// Decode-sized attention (Tq <= 4): split-K over the key range, then an LSE-weighted merge.
+// Decode-sized attention (Tq <= 4, Tq * Hq/Hkv <= 16 query rows per KV head): split-K over the
+// key range with the LSE-weighted merge of the splits done in the same launch.
 //
 // Each decode step i attends its single new query to the active prefix kv_len = T + i + 1
 // (fish-speech PR #1312 "perf(text2semantic): pass only active KV cache prefix to SDPA",
-// section Change); the step reads 2*kv_len*Hkv*D*elem bytes of K/V and does almost no math
-// per byte, so the kernel is built to stream K/V at HBM rate:
-//   * one workgroup per (split, KV head, batch element); the key range [0, visit) is cut into
-//     gridDim.x equal parts computed on the device from kv_len, so a fixed grid (graph replay
-//     with a device kv_len) still spreads any length over every workgroup;
-//   * all query rows of a GQA group (Hq/Hkv heads x Tq rows, <= 16) share each K/V load:
-//     S = Q K^T on v_mfma_f32_16x16x32 (K straight from global memory in the B-operand
-//     layout, the group's query rows as A), softmax in fp32, and P V on the vector ALUs with
-//     P kept in fp32 (each lane owns 8 output columns of a quarter of the keys);
-//   * a workgroup of 4 wavefronts takes one split; its wavefronts merge in LDS. With several
-//     splits, each workgroup writes its unnormalised (m, l, o) to the caller's workspace and a
-//     second launch merges them with weights exp(m_s - max m).
+// section Change). A step reads 2*kv_len*Hkv*D*elem bytes of K/V and does little math per
+// byte; at the lengths of a decode job it is bound by the chain of dependent steps (cursor ->
+// loads -> math -> merge), so the kernel keeps that chain short and spreads the loads over
+// many CUs:
+//   * one workgroup of 4 wavefronts per (split, KV head g, batch element b); the split's key
+//     range is dealt out to the wavefronts in 16-key tiles, and each wavefront loads its next
+//     tile while it works on the current one;
+//   * the query rows of a GQA group (R = Tq * Hq/Hkv <= 16, padded to 16) share each K/V load.
+//     S^T = K Q^T runs on v_mfma_f32_16x16x32 with K straight from global memory as the A
+//     operand; its accumulator leaves, in each lane, four keys of one query row -- exactly the
+//     A-operand layout of v_mfma_f32_16x16x16, so P V runs on the matrix cores with P staying
+//     in the lane that computed it. V^T operands come from a small per-wavefront LDS tile by
+//     transposed reads (ds_read_b64_tr_b16);
+//   * online softmax in fp32 with exp2 (scale folded), the row max over a tile by two
+//     cross-lane exchanges; the reference max moves only when a tile's max passes it by more
+//     than 2^8 in probability (the stale reference cancels in O / l);
+//   * the 4 wavefronts merge through LDS; with several splits each workgroup stores its
+//     unnormalised (m, l, o) to the caller's workspace with device-coherent (sc1) stores --
+//     the form agent-scope atomic stores take, visible to any XCD once complete -- and counts
+//     itself in; the last workgroup of (b, g) to arrive acquires (agent-scope fence) and merges
+//     the splits with weights exp(m_s - max m), then writes the output.
+#include <type_traits>
+
 #include "common.h"
 
 namespace skv {
 
-template <typename T> struct Mfma16;
-template <> struct Mfma16<bf16_t> {
-  typedef bf16x8 vec;
-  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short dec_s16x4;
+typedef __attribute__((address_space(3))) dec_s16x4 dec_lds_s16x4;
+
+template <typename T> struct DecMma;
+template <> struct DecMma<bf16_t> {
+  typedef bf16x8 vec8;
+  typedef dec_s16x4 vec4;
+  static __device__ __forceinline__ f32x4 qk(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 pv(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec4 pack(float x0, float x1, float x2, float x3) {
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 b4;
+    const b4 v = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+    return __builtin_bit_cast(vec4, v);
+  }
+  // running sum plus the four rounded values (two dot2 with (1, 1))
+  static __device__ __forceinline__ float sum4(vec4 p, float acc) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 b2;
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 b4;
+    const b4 v = __builtin_bit_cast(b4, p);
+    const b2 one = {(__bf16)1.f, (__bf16)1.f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(b2{v[0], v[1]}, one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(b2{v[2], v[3]}, one, acc, false);
+  }
 };
-template <> struct Mfma16<f16_t> {
-  typedef f16x8 vec;
-  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+template <> struct DecMma<f16_t> {
+  typedef f16x8 vec8;
+  typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 vec4;
+  static __device__ __forceinline__ f32x4 qk(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec4 pack(float x0, float x1, float x2, float x3) {
+    return vec4{(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
+  }
+  static __device__ __forceinline__ float sum4(vec4 p, float acc) {
+    typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 h2;
+    const h2 one = {(_Float16)1.f, (_Float16)1.f};
+    acc = __builtin_amdgcn_fdot2(h2{p[0], p[1]}, one, acc, false);
+    return __builtin_amdgcn_fdot2(h2{p[2], p[3]}, one, acc, false);
   }
 };
 
-constexpr int kDecBN = 64;   // keys per tile
-constexpr int kDecRows = 16; // row slots per (b, KV head) in the workspace
+constexpr int kDecWaves = 4;    // wavefronts per workgroup
+constexpr int kDecTile = 16;    // keys per wavefront tile (one MFMA block of keys)
+constexpr int kDecChunk = kDecWaves * kDecTile;  // keys per workgroup round; splits are whole chunks
+constexpr int kDecRows = 16;    // query rows per KV head (MFMA block; R <= 16 are used)
+constexpr int kDecMaxSplits = 64;
+constexpr float kDecRescaleLog2 = 8.f;
 
 __host__ __device__ __forceinline__ size_t dec_counter_floats(int B, int Hkv) {
   return (((size_t)B * Hkv + 1 + 63) / 64) * 64;  // B*Hkv split counters + 1, 256-byte multiple
 }
 __host__ __device__ __forceinline__ size_t dec_o_floats(int B, int Hkv, int D, int n_splits) {
-  return (size_t)B * Hkv * kDecRows * n_splits * D;
+  return (size_t)B * Hkv * n_splits * kDecRows * D;
 }
 __host__ __device__ __forceinline__ size_t dec_ml_floats(int B, int Hkv, int n_splits) {
-  return ((size_t)B * Hkv * kDecRows * n_splits * 2 + 3) & ~(size_t)3;  // keep 16-byte alignment
+  return ((size_t)B * Hkv * n_splits * kDecRows * 2 + 3) & ~(size_t)3;  // keep 16-byte alignment
 }
-
-__device__ __forceinline__ size_t dec_part_index(int b, int g, int r, int split, int Hkv,
+// partial of query row r from split `split` of (b, g)
+__device__ __forceinline__ size_t dec_part_index(int b, int g, int split, int r, int Hkv,
                                                  int n_splits) {
-  return (((size_t)b * Hkv + g) * kDecRows + r) * n_splits + split;
+  return (((size_t)b * Hkv + g) * n_splits + split) * kDecRows + r;
 }
 
-template <typename T>
-__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
-  const T* e = (const T*)&u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = to_f32(e[i]);
+// Split partials cross XCDs, whose L2 caches are not coherent with each other. They are
+// stored and loaded with the sc1 cache policy -- device-coherent, as agent-scope atomic
+// stores and loads are -- so a store that has completed (vmcnt drained) is visible to a later
+// sc1 load from any CU, with no cache write-back or invalidate.
+constexpr int kDeviceCoherent = 16;  // buffer-op cache policy bits: sc1
+constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0)
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* base, size_t floats) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(floats * sizeof(float)),
+                                           0x00020000);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, size_t fidx, float4 v) {
+  const u32x4 d = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                   __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, size_t fidx, float2 v) {
+  const u32x2 d = {__float_as_uint(v.x), __float_as_uint(v.y)};
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent);
+}
+__device__ __forceinline__ float4 load_coherent4(__amdgpu_buffer_rsrc_t r, size_t fidx) {
+  const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent);
+  return make_float4(__uint_as_float(d[0]), __uint_as_float(d[1]), __uint_as_float(d[2]),
+                     __uint_as_float(d[3]));
+}
+__device__ __forceinline__ float2 load_coherent2(__amdgpu_buffer_rsrc_t r, size_t fidx) {
+  const u32x2 d = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent);
+  return make_float2(__uint_as_float(d[0]), __uint_as_float(d[1]));
 }
 
-constexpr int kDecWaves = 4;  // wavefronts per workgroup; they share one split's tiles
-// Per-lane merge state in the "row layout": row r0 + lane/16, columns [8*(lane%16), +8).
+// Online-softmax state of one query row over 8 output columns.
 struct MergeState {
   float M, L, o[8];
 };
@@ -70,141 +143,177 @@ __device__ __forceinline__ void merge_init(MergeState& st) {
   for (int e = 0; e < 8; ++e) st.o[e] = 0.f;
 }
 
-// Fold a partial (m, l, o) into st with weights exp2((m - M) * c2) (online, max-safe).
-__device__ __forceinline__ void merge_add(MergeState& st, float m, float l, const float* o,
-                                          float c2) {
-  const float m_new = fmaxf(st.M, m);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float wa = __builtin_amdgcn_exp2f((st.M - m_use) * c2);
-  const float wb = __builtin_amdgcn_exp2f((m - m_use) * c2);
-  st.L = st.L * wa + l * wb;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) st.o[e] = st.o[e] * wa + o[e] * wb;
-  st.M = m_new;
-}
-
-// LDS staging of one state per (wavefront, row): m, l and D output columns.
-template <int D, int NR>
-struct DecStage {
-  float m[kDecWaves][NR];
-  float l[kDecWaves][NR];
-  float o[kDecWaves][NR][D];
-};
-
-// Combine the kDecWaves staged states of row r, columns [8dc, 8dc+8).
-template <int D, int NR>
-__device__ __forceinline__ void combine_staged(const DecStage<D, NR>& sg, int r, int dc,
-                                               float c2, MergeState& st) {
-  merge_init(st);
-#pragma unroll
-  for (int w = 0; w < kDecWaves; ++w) {
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = dc < D / 8 ? sg.o[w][r][8 * dc + e] : 0.f;
-    merge_add(st, sg.m[w][r], sg.l[w][r], o, c2);
-  }
-}
-
+// Output row r (= t * group + hh: query t, head g * group + hh), columns [8dc, 8dc + 8).
 template <typename OutT>
 __device__ __forceinline__ void write_row(const AttnArgs& a, int D, int group, int b, int g, int r,
                                           int dc, const MergeState& st) {
   const int t = r / group, h = g * group + (r - t * group);
   const float inv = st.L > 0.f ? 1.f / st.L : 0.f;  // L = 0: the batch element was rejected
-  if (dc < D / 8) {
-    OutT* out = (OutT*)a.out + (((int64_t)b * a.Tq + t) * a.Hq + h) * D + 8 * dc;
+  OutT* out = (OutT*)a.out + (((int64_t)b * a.Tq + t) * a.Hq + h) * D + 8 * dc;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = from_f32<OutT>(st.o[e] * inv);
-  }
+  for (int e = 0; e < 8; ++e) out[e] = from_f32<OutT>(st.o[e] * inv);
   if (a.lse && dc == 0)
     a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = st.L > 0.f ? st.M * a.scale + logf(st.L) : -INFINITY;
 }
 
-// The workgroup merges the n_splits partials of the R rows of (b, g) and writes the outputs:
-// wavefront w folds splits w, w + kDecWaves, ... (loads of 8 splits at a time, nothing
-// branching on loaded data), then wavefront 0 combines the kDecWaves states through LDS.
-template <int D, int NR, typename OutT>
-__device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, const float* ws_o,
-                                             const float* ws_ml, DecStage<D, NR>& sg, int b, int g,
-                                             int n_splits) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int dc = lane & 15;
-  const bool dc_ok = dc < D / 8;
-  const int R = a.Tq * group;
-  const float c2 = a.scale_log2;
-    for (int r0 = 0; r0 < NR; r0 += 4) {
-      const int r = r0 + (lane >> 4);
-      const bool row_ok = r < R;
-      const size_t p0 = dec_part_index(b, g, row_ok ? r : 0, 0, a.Hkv, n_splits);
-      MergeState st;
-      merge_init(st);
-      constexpr int kBatch = 8;
-      for (int s0 = wave; s0 < n_splits; s0 += kBatch * kDecWaves) {
-        float2 ml[kBatch];
-        float4 oa[kBatch], ob[kBatch];
+// Fold N partials (m, l, o) into st: the new max first, then independent weights and sums
+// (no chain of per-partial rescales).
+template <int N>
+__device__ __forceinline__ void fold_batch(MergeState& st, const float2* ml, const float4* oa,
+                                           const float4* ob, float c2) {
+  float mb = st.M;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int sp = s0 + u * kDecWaves;
-          const bool ok = sp < n_splits;
-          ml[u] = ok ? *(const float2*)(ws_ml + 2 * (p0 + sp)) : make_float2(-INFINITY, 0.f);
-          const float* po = ws_o + (p0 + (ok ? sp : 0)) * D + 8 * dc;
-          oa[u] = (ok && dc_ok) ? *(const float4*)po : make_float4(0.f, 0.f, 0.f, 0.f);
-          ob[u] = (ok && dc_ok) ? *(const float4*)(po + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+  for (int u = 0; u < N; ++u) mb = fmaxf(mb, ml[u].x);
+  const float m_use = mb == -INFINITY ? 0.f : mb;
+  const float ws = __builtin_amdgcn_exp2f((st.M - m_use) * c2);
+  float L = st.L * ws, o[8];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const float o8[8] = {oa[u].x, oa[u].y, oa[u].z, oa[u].w, ob[u].x, ob[u].y, ob[u].z, ob[u].w};
-          merge_add(st, ml[u].x, ml[u].y, o8, c2);
-        }
-      }
-      __syncthreads();  // the previous pass's reads of the staging area are done
-      if (row_ok) {
-        if (dc == 0) {
-          sg.m[wave][r] = st.M;
-          sg.l[wave][r] = st.L;
-        }
-        if (dc_ok)
+  for (int e = 0; e < 8; ++e) o[e] = st.o[e] * ws;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sg.o[wave][r][8 * dc + e] = st.o[e];
-      }
-      __syncthreads();
-      if (wave == 0 && row_ok) {
-        MergeState fin;
-        combine_staged<D, NR>(sg, r, dc, c2, fin);
-        write_row<OutT>(a, D, group, b, g, r, dc, fin);
-      }
-    }
+  for (int u = 0; u < N; ++u) {
+    const float w = __builtin_amdgcn_exp2f((ml[u].x - m_use) * c2);
+    L = fmaf(w, ml[u].y, L);
+    o[0] = fmaf(w, oa[u].x, o[0]);
+    o[1] = fmaf(w, oa[u].y, o[1]);
+    o[2] = fmaf(w, oa[u].z, o[2]);
+    o[3] = fmaf(w, oa[u].w, o[3]);
+    o[4] = fmaf(w, ob[u].x, o[4]);
+    o[5] = fmaf(w, ob[u].y, o[5]);
+    o[6] = fmaf(w, ob[u].z, o[6]);
+    o[7] = fmaf(w, ob[u].w, o[7]);
+  }
+  st.M = mb;
+  st.L = L;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.o[e] = o[e];
 }
 
-// NR: query rows per KV head rounded up to 4, 8 or 16 (R = Tq * Hq/Hkv <= NR).
-// Workgroup = kDecWaves wavefronts per (split, KV head g, batch element b); the split's key
-// range is cut into 64-key tiles dealt round-robin to the wavefronts. Each wavefront keeps its
-// own online-softmax state; the workgroup merges them in LDS. With one split that is the
-// output; otherwise the workgroup's partial goes to the workspace and k_decode_merge, a second
-// launch, merges the splits. (Merging in this launch, by the last workgroup to arrive, needs a
-// release fence per workgroup -- an L2 write-back on this multi-XCD chip -- and measured slower
-// than the second launch at every length tried, 64 to 32768 keys.)
+// The last workgroup of (b, g), after its acquire: fold the n_splits partials of each used
+// row with ordinary (cached) loads. Thread t takes
+// (row, 8-column chunk) pair t / tpp and every tpp-th split from t % tpp; the tpp threads of a
+// pair (adjacent lanes of one wavefront) then combine by lane exchanges.
+template <int D, typename OutT>
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, const float* ws_o,
+                                             const float* ws_ml, int b, int g, int n_splits) {
+  constexpr int CH = D / 8;  // 8-column chunks per row
+  const int R = a.Tq * group;
+  int rp = 1;
+  while (rp < R) rp <<= 1;   // rows padded to a power of two: pairs divide 256
+  const int tpp = 256 / (rp * CH) > 1 ? 256 / (rp * CH) : 1;
+  const int t = threadIdx.x;
+  const int pair = t / tpp, sub = t - pair * tpp;
+  const int r = pair / CH, dc = pair - r * CH;
+  const bool row_ok = r < R;
+  const float c2 = a.scale_log2;
+  MergeState st;
+  merge_init(st);
+  constexpr int kBatch = 8;
+  for (int s0 = sub; s0 < n_splits; s0 += kBatch * tpp) {
+    float2 ml[kBatch];
+    float4 oa[kBatch], ob[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {  // every load of the batch issued before any use
+      const int sp = s0 + u * tpp;
+      const bool ok = row_ok && sp < n_splits;
+      const size_t pi = dec_part_index(b, g, ok ? sp : 0, ok ? r : 0, a.Hkv, n_splits);
+      ml[u] = *(const float2*)(ws_ml + 2 * pi);
+      oa[u] = *(const float4*)(ws_o + pi * D + 8 * dc);
+      ob[u] = *(const float4*)(ws_o + pi * D + 8 * dc + 4);
+      if (!ok) {  // contributes weight 0 and finite values only
+        ml[u] = make_float2(-INFINITY, 0.f);
+        oa[u] = ob[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    fold_batch<kBatch>(st, ml, oa, ob, c2);
+  }
+  // the tpp threads of a pair: common max first, then plain sums of the rescaled states
+  float M = st.M;
+  for (int off = tpp >> 1; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  {
+    const float w = __builtin_amdgcn_exp2f((st.M - (M == -INFINITY ? 0.f : M)) * c2);
+    st.L *= w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[e] *= w;
+    st.M = M;
+  }
+  for (int off = tpp >> 1; off > 0; off >>= 1) {
+    st.L += __shfl_xor(st.L, off, 64);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.o[e] += __shfl_xor(st.o[e], off, 64);
+  }
+  if (row_ok && sub == 0) write_row<OutT>(a, D, group, b, g, r, dc, st);
+}
+
+// Workgroup = kDecWaves wavefronts per (split, KV head g, batch element b). The split covers
+// whole 64-key chunks of the visited range; wavefront w takes the 16-key tiles at offsets
+// 16w, 16w + 64, ... of it.
 // FUSED: one launch per decode step with the write cursor on the device (attn_decode_step):
 // c = *cursor; the new rows k_new/v_new [B, Tq, Hkv, D] are written to cache rows c .. c+Tq-1
 // and attended over as keys c .. c+Tq-1 straight from the sources (no wavefront of this launch
 // reads a cache row another one writes); the last (b, g) to finish sets *cursor = c+Tq and
 // kv_len_out[:] = c+Tq, after every wavefront has read the cursor.
-template <typename T, int D, int NR, typename OutT, bool FUSED>
+template <typename T, int D, typename OutT, bool FUSED>
 __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int group, float* ws,
                                                                 int n_splits) {
-  typedef typename Mfma16<T>::vec vec;
-  constexpr int DQ = D / 32;  // 32-wide d chunks of the QK^T contraction
-  __shared__ __attribute__((aligned(16))) float P[kDecWaves][kDecBN][kDecRows];
-  __shared__ float alpha_s[kDecWaves][kDecRows];
-  __shared__ __attribute__((aligned(16))) DecStage<D, NR> sg;
+  // P V in fp16 (V converted while staged) for bf16 inputs with an fp32 output, where a
+  // bf16-rounded P would be the dominant error of the result
+  constexpr bool PV16 = std::is_same<T, bf16_t>::value && std::is_same<OutT, float>::value;
+  typedef typename std::conditional<PV16, f16_t, T>::type TP;
+  typedef DecMma<T> MQ;
+  typedef DecMma<TP> MP;
+  typedef typename MQ::vec8 vec8;
+  typedef typename MP::vec4 pvec4;
+  constexpr int DQ = D / 32;   // 32-wide d steps of S^T
+  constexpr int CB = D / 16;   // 16-column output blocks
+  constexpr int VU = D / 32;   // 16-byte V pieces per lane per tile
+  constexpr int CH = D / 8;    // 8-column chunks per row
+  // V tile row pitch: 32 bytes past a multiple of 256, so the 8 key rows one half-wavefront
+  // reads in a transposed read fall on distinct banks
+  constexpr int LDV = D == 128 ? D + 16 : D + 80;
+  __shared__ __attribute__((aligned(16))) union {
+    TP v[kDecWaves][kDecTile * LDV];     // per-wavefront V tile
+    float o[kDecWaves][kDecRows][D];     // after the tile loop: per-wavefront outputs
+  } sm;
+  __shared__ float st_m[kDecWaves][kDecRows], st_l[kDecWaves][kDecRows];
+  __shared__ int last_s;
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // Workgroup -> (split, b, g). Dispatch deals consecutive workgroup ids to the 8 XCDs in turn;
+  // when B*Hkv is a multiple of 8, the ids are arranged so that every split of one (b, g)
+  // lands on the same XCD and its partials meet in one L2.
+  const int BH = a.B * a.Hkv;
+  int split, bg;
+  if ((BH & 7) == 0) {
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    const int kq = k / n_splits;
+    bg = x + 8 * kq;
+    split = k - kq * n_splits;
+  } else {
+    bg = blockIdx.x / n_splits;
+    split = blockIdx.x - bg * n_splits;
+  }
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 15, quad = lane >> 4;
+  const int n16 = lane & 15, G = lane >> 4;
   const int R = a.Tq * group;
   // workspace: arrival counters first (a fixed place for any split count), then partials
   int* counters = (int*)ws;
   float* ws_o = ws + dec_counter_floats(a.B, a.Hkv);
   float* ws_ml = ws_o + dec_o_floats(a.B, a.Hkv, D, n_splits);
+
+  // query row n16 as the B operand of S^T (independent of the metadata: issued first)
+  vec8 qb[DQ];
+  {
+    const int r = n16;
+    if (r < R) {
+      const int t = r / group, hh = r - t * group;
+      const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + t) * a.Hq + g * group + hh) * D + 8 * G;
+#pragma unroll
+      for (int c = 0; c < DQ; ++c) qb[c] = *(const vec8*)(qp + 32 * c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < DQ; ++c) qb[c] = vec8{};
+    }
+  }
 
   // a rejected batch element still takes part in the arrival count, with empty splits
   int cur = 0;  // fused step: the write position of this step
@@ -221,51 +330,17 @@ __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int 
     ks = key_set(a, b);
     if (!ks.ok && threadIdx.x == 0 && split == 0 && g == 0) report(a.err, dev_error_bit(a));
   }
-  // this split's share of the visited rows, in whole 64-key tiles
+  // this split's share of the visited rows, in whole 64-key chunks
   int per = (ks.visit + n_splits - 1) / n_splits;
-  per = (per + kDecBN - 1) & ~(kDecBN - 1);
+  per = (per + kDecChunk - 1) / kDecChunk * kDecChunk;
   const int start = split * per;
   const int end = ks.ok ? min(ks.visit, start + per) : 0;
-
-  // A operand: query row `col` (row r = t*group + hh -> head g*group + hh, query t)
-  vec qa[DQ];
-  {
-    const int r = col;
-    if (r < R) {  // independent of kv_len, so these loads overlap the metadata load
-      const int t = r / group, hh = r - t * group;
-      const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + t) * a.Hq + g * group + hh) * D + 8 * quad;
-#pragma unroll
-      for (int c = 0; c < DQ; ++c) qa[c] = *(const vec*)(qp + 32 * c);
-    } else {
-#pragma unroll
-      for (int c = 0; c < DQ; ++c) qa[c] = vec{};
-    }
+  // last visible key of row n16 within this split (padding rows see the whole split)
+  int lim = end - 1;
+  if (n16 < R) {
+    const int rl = row_limit(a.mask, a.block, ks.len - a.Tq + n16 / group, ks.len);
+    lim = rl < lim ? rl : lim;
   }
-  // accumulator rows held by this lane in the S phase: r = 4*quad + j
-  int pos[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 4 * quad + j;
-    pos[j] = ks.len - a.Tq + (r < R ? r / group : 0);
-  }
-  // last visible key of each row within this split: one compare per score, no branches
-  int lim[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rl = row_limit(a.mask, a.block, pos[j], ks.len);
-    lim[j] = rl < end - 1 ? rl : end - 1;
-  }
-  float m[4], l[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-  }
-  float acc[NR][8];
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
 
   const int64_t rstride = (int64_t)a.Hkv * D;
   const T* kbase = (const T*)a.k + ks.base_row * rstride + (int64_t)g * D;
@@ -288,165 +363,171 @@ __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int 
       }
     }
   }
-  const float c2 = a.scale_log2;
-  const int dc = col;    // PV phase: this lane's 8 output columns [8dc, 8dc+8)
-  const int kg = quad;   // PV phase: keys kg, kg+4, ..., kg+60 of the tile
-  const bool dc_ok = dc < D / 8;  // D = 64 leaves half of the lanes without columns
-  float (*Pw)[kDecRows] = P[wave];
 
-  // the wavefronts of the workgroup take the split's tiles in turn; no workgroup barrier in
-  // here (trip counts differ): P and alpha_s are per wavefront
-  for (int tile = start + kDecBN * wave; tile < end; tile += kDecBN * kDecWaves) {
-    // issue every K and V load of the tile first
-    uint4 kraw[4][DQ];
+  // Tile loads. K: lane (G, n16) takes key tile + n16, d = 32c + 8G .. +8 (the A operand of
+  // S^T). V: lane takes key tile + lane/4, d = 8(4u + lane%4) .. +8 (whole rows per 4 lanes).
+  // Keys at or past `end` read as zero and issue no load.
+  auto load_tile = [&](int tile, uint4* kr, uint4* vr) {
+    const int jk = tile + n16;
+    const T* kp = (FUSED && jk >= cur) ? knew : kbase;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int j = tile + 16 * kb + col;
-      const T* kb_ptr = (FUSED && j >= cur) ? knew : kbase;
+    for (int c = 0; c < DQ; ++c)
+      kr[c] = jk < end ? *(const uint4*)(kp + (int64_t)jk * rstride + 32 * c + 8 * G)
+                       : make_uint4(0, 0, 0, 0);
+    const int jv = tile + (lane >> 2);
+    const T* vp = (FUSED && jv >= cur) ? vnew : vbase;
 #pragma unroll
-      for (int c = 0; c < DQ; ++c)
-        kraw[kb][c] = j < end ? *(const uint4*)(kb_ptr + (int64_t)j * rstride + 32 * c + 8 * quad)
-                              : make_uint4(0, 0, 0, 0);
-    }
-    uint4 vraw[16];
+    for (int u = 0; u < VU; ++u)
+      vr[u] = jv < end ? *(const uint4*)(vp + (int64_t)jv * rstride + 8 * (4 * u + (lane & 3)))
+                       : make_uint4(0, 0, 0, 0);
+  };
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[CB];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = tile + kg + 4 * i;
-      const T* vb_ptr = (FUSED && j >= cur) ? vnew : vbase;
-      vraw[i] = (j < end && dc_ok) ? *(const uint4*)(vb_ptr + (int64_t)j * rstride + 8 * dc)
-                                   : make_uint4(0, 0, 0, 0);
-    }
-    // S = Q K^T: s[kb][j] = score(row 4*quad+j, key tile+16kb+col)
-    f32x4 s[4];
+  for (int cb = 0; cb < CB; ++cb) o[cb] = f32x4{};
+  const float c2 = a.scale_log2;
+  TP* vt = sm.v[wave];
+
+  uint4 kr[DQ], vr[VU];
+  const int t0 = start + kDecTile * wave;
+  load_tile(t0, kr, vr);
+  for (int tile = t0; tile < end; tile += kDecChunk) {
+    uint4 kn[DQ], vn[VU];
+    load_tile(tile + kDecChunk, kn, vn);  // next tile in flight during this one's math
+
+    // V tile to LDS (row = key, converted to the P V type)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4{};
+    for (int u = 0; u < VU; ++u) {
+      TP* dst = vt + (lane >> 2) * LDV + 8 * (4 * u + (lane & 3));
+      if constexpr (PV16) {
+        const bf16_t* e = (const bf16_t*)&vr[u];
+        typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 h8;
+        h8 hv;
 #pragma unroll
-      for (int c = 0; c < DQ; ++c) {
-        vec kv;
-        __builtin_memcpy(&kv, &kraw[kb][c], sizeof(vec));
-        s[kb] = Mfma16<T>::mma(qa[c], kv, s[kb]);
+        for (int k = 0; k < 8; ++k) hv[k] = (f16_t)(float)e[k];
+        *(h8*)dst = hv;
+      } else {
+        *(uint4*)dst = vr[u];
       }
     }
-    float alpha[4];
+
+    // S^T = K Q^T: s[j] = score(key tile + 4G + j, row n16)
+    f32x4 s = f32x4{};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float mt = -INFINITY;
+    for (int c = 0; c < DQ; ++c) s = MQ::qk(__builtin_bit_cast(vec8, kr[c]), qb[c], s);
+    float sv[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int key = tile + 16 * kb + col;
-        const float sv = key <= lim[j] ? s[kb][j] : -INFINITY;
-        s[kb][j] = sv;
-        mt = fmaxf(mt, sv);
-      }
+    for (int j = 0; j < 4; ++j) sv[j] = tile + 4 * G + j <= lim ? s[j] : -INFINITY;
+    float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const bool grow = (mt - m) * c2 > kDecRescaleLog2;  // NaN (no move) when both are -inf
+    const float m_new = grow ? mt : m;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m - m_use) * c2);
+    const float mc = m_use * c2;
+    const pvec4 pa = MP::pack(__builtin_amdgcn_exp2f(fmaf(sv[0], c2, -mc)),
+                              __builtin_amdgcn_exp2f(fmaf(sv[1], c2, -mc)),
+                              __builtin_amdgcn_exp2f(fmaf(sv[2], c2, -mc)),
+                              __builtin_amdgcn_exp2f(fmaf(sv[3], c2, -mc)));
+    lsum = MP::sum4(pa, lsum * alpha);
+    m = m_new;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // O rows 4G + j take the factor of row 4G + j, held by lane 4G + j
+      float al[4];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
-      const float m_new = fmaxf(m[j], mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[j] = __builtin_amdgcn_exp2f((m[j] - m_use) * c2);
-      const float mc = m_use * c2;
-      float ps = 0.f;
+      for (int j = 0; j < 4; ++j) al[j] = __shfl(alpha, 4 * G + j, 64);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][j], c2, -mc));
-        s[kb][j] = p;
-        ps += p;
-      }
-      l[j] = l[j] * alpha[j] + ps;
-      m[j] = m_new;
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[cb][j] *= al[j];
     }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      *(float4*)&Pw[16 * kb + col][4 * quad] = make_float4(s[kb][0], s[kb][1], s[kb][2], s[kb][3]);
-    if (col == 0)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) alpha_s[wave][4 * quad + j] = alpha[j];
+
+    // P V: B operand V[key 4G + t][16cb + n16], t = 0..3, by one transposed read: lane k of
+    // each 16-lane group points at V[4G + k/4][16cb + 4(k%4)]
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const float al = alpha_s[wave][r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[r][e] *= al;
+    for (int cb = 0; cb < CB; ++cb) {
+      const TP* vp = vt + (4 * G + (n16 >> 2)) * LDV + 16 * cb + 4 * (n16 & 3);
+      const dec_s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dec_lds_s16x4*)vp);
+      o[cb] = MP::pv(pa, __builtin_bit_cast(pvec4, x), o[cb]);
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float v[8];
-      unpack8<T>(vraw[i], v);
-      const float* pr = Pw[kg + 4 * i];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const float p = pr[r];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, v[e], acc[r][e]);
-      }
-    }
-    // P and alpha_s are rewritten by the next tile of this wavefront
+    // the V tile is rewritten by the next iteration of this wavefront
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int c = 0; c < DQ; ++c) kr[c] = kn[c];
+#pragma unroll
+    for (int u = 0; u < VU; ++u) vr[u] = vn[u];
   }
 
-  // row sums: each of the 16 lanes of a quad holds part of rows 4*quad+j
+  // row n16's sum: the four lane groups hold different keys of it
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  __syncthreads();  // every wavefront is done with its V tile: the union becomes the output stage
+  if (G == 0) {
+    st_m[wave][n16] = m;
+    st_l[wave][n16] = lsum;
+  }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) l[j] += __shfl_xor(l[j], o, 64);
-  // outputs: the four key groups (lane bits 4-5) hold partial sums of the same columns
-#pragma unroll
-  for (int r = 0; r < NR; ++r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[r][e] += __shfl_xor(acc[r][e], 16, 64);
-      acc[r][e] += __shfl_xor(acc[r][e], 32, 64);
-    }
-  // stage this wavefront's state, then merge the workgroup's wavefronts row by row
-  if (col == 0)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (4 * quad + j < NR) {
-        sg.m[wave][4 * quad + j] = m[j];
-        sg.l[wave][4 * quad + j] = l[j];
-      }
-  if (kg == 0 && dc_ok)
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sg.o[wave][r][8 * dc + e] = acc[r][e];
+    for (int j = 0; j < 4; ++j) sm.o[wave][4 * G + j][16 * cb + n16] = o[cb][j];
   __syncthreads();
 
+  // merge the wavefronts: thread -> (row, 8-column chunk); 256 threads cover 16 rows x D/8
+  const int r = threadIdx.x / CH, dc = threadIdx.x - r * CH;
+  const bool mine = r < R;
+  MergeState st;
+  merge_init(st);
+  if (mine) {
+    float2 ml[kDecWaves];
+    float4 oa[kDecWaves], ob[kDecWaves];
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      ml[w] = make_float2(st_m[w][r], st_l[w][r]);
+      oa[w] = *(const float4*)&sm.o[w][r][8 * dc];
+      ob[w] = *(const float4*)&sm.o[w][r][8 * dc + 4];
+    }
+    fold_batch<kDecWaves>(st, ml, oa, ob, c2);
+  }
+
   if (n_splits == 1) {  // the workgroup saw every key: its merge is the output
-    if (wave == 0)
-      for (int r0 = 0; r0 < R; r0 += 4) {
-        const int r = r0 + (lane >> 4);
-        MergeState st;
-        if (r < R) {
-          combine_staged<D, NR>(sg, r, dc, c2, st);
-          write_row<OutT>(a, D, group, b, g, r, dc, st);
-        }
-      }
+    if (mine) write_row<OutT>(a, D, group, b, g, r, dc, st);
   } else {
-    // the workgroup's partial goes to the workspace
-    if (wave == 0)
-      for (int r0 = 0; r0 < R; r0 += 4) {
-        const int r = r0 + (lane >> 4);
-        if (r >= R) continue;
-        MergeState st;
-        combine_staged<D, NR>(sg, r, dc, c2, st);
-        const size_t pi = dec_part_index(b, g, r, split, a.Hkv, n_splits);
-        if (dc_ok) {
-          float* po = ws_o + pi * D + 8 * dc;
-          *(float4*)po = make_float4(st.o[0], st.o[1], st.o[2], st.o[3]);
-          *(float4*)(po + 4) = make_float4(st.o[4], st.o[5], st.o[6], st.o[7]);
-        }
-        if (dc == 0) *(float2*)(ws_ml + 2 * pi) = make_float2(st.M, st.L);
-      }
-    return;  // k_decode_merge finishes the step
+    const __amdgpu_buffer_rsrc_t ro = ws_rsrc(ws_o, dec_o_floats(a.B, a.Hkv, D, n_splits));
+    const __amdgpu_buffer_rsrc_t rml = ws_rsrc(ws_ml, dec_ml_floats(a.B, a.Hkv, n_splits));
+    if (mine) {
+      const size_t pi = dec_part_index(b, g, split, r, a.Hkv, n_splits);
+      store_coherent(ro, pi * D + 8 * dc, make_float4(st.o[0], st.o[1], st.o[2], st.o[3]));
+      store_coherent(ro, pi * D + 8 * dc + 4, make_float4(st.o[4], st.o[5], st.o[6], st.o[7]));
+      if (dc == 0) store_coherent(rml, 2 * pi, make_float2(st.M, st.L));
+    }
+    // every store of the workgroup has completed before its arrival is counted
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int* cnt = &counters[b * a.Hkv + g];
+      const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == n_splits - 1;
+      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_s = last;
+    }
+    __syncthreads();
+    if (!last_s) return;
+    // acquire at agent scope: drop cached copies (L1, and L2 lines another XCD may have
+    // rewritten) so the loads below see every split's completed stores
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    merge_splits<D, OutT>(a, group, ws_o, ws_ml, b, g, n_splits);
   }
   if constexpr (FUSED) {
-    // one split per (b, g): every workgroup of the launch read the cursor before it got here,
-    // so the last one to finish may move it (an arrival count only; no data is handed over)
+    // this workgroup wrote (b, g)'s output; every workgroup of the launch read the cursor
+    // before it got this far, so the last (b, g) to finish may move it (an arrival count
+    // only; no data is handed over)
     if (threadIdx.x == 0) {
       const int old = __hip_atomic_fetch_add(&counters[a.B * a.Hkv], 1, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
@@ -462,36 +543,15 @@ __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int 
   }
 }
 
-// Second launch of the two-kernel variant: one workgroup per (b, KV head) merges the splits.
-// In the fused step, workgroup (0, 0) also moves the cursor: every workgroup of the first
-// launch read it before this launch started, and no workgroup of this one reads it otherwise.
-template <int D, int NR, typename OutT, bool FUSED>
-__global__ void __launch_bounds__(64 * kDecWaves) k_decode_merge(AttnArgs a, int group, float* ws,
-                                                                 int n_splits) {
-  __shared__ __attribute__((aligned(16))) DecStage<D, NR> sg;
-  const int g = blockIdx.x, b = blockIdx.y;
-  const float* ws_o = ws + dec_counter_floats(a.B, a.Hkv);
-  const float* ws_ml = ws_o + dec_o_floats(a.B, a.Hkv, D, n_splits);
-  merge_splits<D, NR, OutT>(a, group, ws_o, ws_ml, sg, b, g, n_splits);
-  if constexpr (FUSED) {
-    if (b == 0 && g == 0 && threadIdx.x == 0) {
-      const int cur = *a.cursor;
-      if (cur >= 0 && (int64_t)cur + a.Tq <= a.cap) {
-        if (a.kv_len_out)
-          for (int bb = 0; bb < a.B; ++bb) a.kv_len_out[bb] = cur + a.Tq;
-        *a.cursor = cur + a.Tq;
-      }
-    }
-  }
-}
-
-// Split count used by both the launcher and the workspace query.
+// Split count used by both the launcher and the workspace query: one 64-key chunk per split
+// at least, about two workgroups per CU over the chip, and no more splits than the merge folds
+// in two rounds of loads.
 int decode_splits(int B, int Hkv, int max_len) {
-  const int tiles = (max_len + kDecBN - 1) / kDecBN;
-  const int by_tiles = (tiles + kDecWaves - 1) / kDecWaves;  // one tile per wavefront at most
-  int target = 2048 / (B * Hkv * kDecWaves);  // about two wavefronts per SIMD over the chip
+  const int chunks = (max_len + kDecChunk - 1) / kDecChunk;
+  int target = 512 / (B * Hkv);
   if (target < 1) target = 1;
-  int s = by_tiles < target ? by_tiles : target;
+  int s = chunks < target ? chunks : target;
+  if (s > kDecMaxSplits) s = kDecMaxSplits;
   return s < 1 ? 1 : s;
 }
 
@@ -500,25 +560,14 @@ size_t decode_workspace_bytes(int B, int Hkv, int D, int n_splits) {
           dec_ml_floats(B, Hkv, n_splits)) * sizeof(float);
 }
 
-template <typename T, int D, int NR, typename OutT, bool FUSED>
-static hipError_t launch_decode_nr(const AttnArgs& a, int group, float* ws, int n_splits,
-                                   hipStream_t s) {
-  dim3 grid(n_splits, a.Hkv, a.B), block(64 * kDecWaves);
-  hipLaunchKernelGGL((k_attn_decode<T, D, NR, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n_splits == 1) return e;
-  hipLaunchKernelGGL((k_decode_merge<D, NR, OutT, FUSED>), dim3(a.Hkv, a.B), block, 0, s, a, group, ws,
-                     n_splits);
-  return hipGetLastError();
-}
-
 template <typename T, int D, typename OutT, bool FUSED>
 static hipError_t launch_decode_f(const AttnArgs& a, int group, float* ws, int n_splits,
                                   hipStream_t s) {
-  const int R = a.Tq * group;
-  if (R <= 4) return launch_decode_nr<T, D, 4, OutT, FUSED>(a, group, ws, n_splits, s);
-  if (R <= 8) return launch_decode_nr<T, D, 8, OutT, FUSED>(a, group, ws, n_splits, s);
-  return launch_decode_nr<T, D, 16, OutT, FUSED>(a, group, ws, n_splits, s);
+  const int64_t blocks = (int64_t)n_splits * a.B * a.Hkv;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)blocks), block(64 * kDecWaves);
+  hipLaunchKernelGGL((k_attn_decode<T, D, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
+  return hipGetLastError();
 }
 
 template <typename T, int D, typename OutT>
