@@ -82,7 +82,7 @@ constexpr int kDecWaves = 4;    // wavefronts per workgroup
 constexpr int kDecTile = 16;    // keys per wavefront tile (one MFMA block of keys)
 constexpr int kDecChunk = kDecWaves * kDecTile;  // keys per workgroup round; splits are whole chunks
 constexpr int kDecRows = 16;    // query rows per KV head (MFMA block; R <= 16 are used)
-constexpr int kDecMaxSplits = 64;
+constexpr int kDecMaxSplits = 32;
 constexpr float kDecRescaleLog2 = 8.f;
 
 __host__ __device__ __forceinline__ size_t dec_counter_floats(int B, int Hkv) {
@@ -543,14 +543,16 @@ __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int 
   }
 }
 
-// Split count used by both the launcher and the workspace query: one 64-key chunk per split
-// at least, about two workgroups per CU over the chip, and no more splits than the merge folds
-// in two rounds of loads.
+// Split count used by both the launcher and the workspace query. A split costs one merge
+// round trip, and too few keys per workgroup leave its loads latency-bound: about 128 keys per
+// split, about one workgroup per CU over the chip, and at most 32 splits (fewer, longer splits
+// measured faster from 1K to 32K keys, where the merge of up to 64 partials cost more than the
+// extra parallelism gave).
 int decode_splits(int B, int Hkv, int max_len) {
-  const int chunks = (max_len + kDecChunk - 1) / kDecChunk;
-  int target = 512 / (B * Hkv);
+  const int by_len = (max_len + 2 * kDecChunk - 1) / (2 * kDecChunk);
+  int target = 256 / (B * Hkv);
   if (target < 1) target = 1;
-  int s = chunks < target ? chunks : target;
+  int s = by_len < target ? by_len : target;
   if (s > kDecMaxSplits) s = kDecMaxSplits;
   return s < 1 ? 1 : s;
 }
