@@ -12,20 +12,25 @@
 //     v_mfma_f32_32x32x16_{bf16,f16}: A = a 32-key slice of the K tile (LDS), B = its queries
 //     (registers, loaded once). In the 32x32 accumulator a lane holds one query column and 16
 //     of the 32 keys, so the row max / row sum need only in-lane work plus one exchange with
-//     lane^32.
+//     lane^32 (v_permlane32_swap).
 //   * Online softmax in fp32 with exp2 and the scale folded into one FMA per score; masked
 //     entries are selected to -inf (never multiplied), so a masked key contributes exactly 0.
 //     The reference max moves (and O is rescaled) only when a tile's max passes it by more than
 //     2^8 in probability; otherwise the rescale factor is exactly 1 and skipped. Row sums add
 //     the rounded probabilities with dot2 instructions.
 //   * O^T += V^T P^T with the same MFMA: P stays in registers (the accumulator's key order is
-//     mapped onto the MFMA's k slots, and V^T is read from LDS in that same order).
-//   * K/V tiles of 64 keys are staged in LDS (K rows padded by 16 bytes, V rows by 64 bytes,
-//     so neither the K reads nor the transposed V reads conflict on the 64 banks); the next
-//     tile's global loads are issued before the current tile's math.
-//   * The two wavefronts sharing a SIMD (one from each of the CU's two workgroups) overlap
-//     matrix-core and vector work: a wavefront raises its priority while it issues MFMAs, so
-//     the other one's softmax fills the vector ALU meanwhile.
+//     mapped onto the MFMA's k slots, and V^T is read from LDS in that same order by
+//     transposed reads, ds_read_b64_tr_b16).
+//   * K/V tiles of 64 keys go from HBM straight into LDS (buffer loads with the lds bit, no
+//     registers in between); 16-byte granules are XOR-swizzled per row so the K reads and the
+//     transposed V reads are free of bank conflicts without padding.
+//   * Software pipeline, one workgroup barrier per tile: K runs one tile ahead of V. While
+//     tile j's softmax runs on the vector ALUs, S^T of tile j+1 is computed on the matrix
+//     cores -- the two streams are interleaved instruction by instruction (scheduling group
+//     barriers), since a wavefront issues in order -- and the loads of V(j+1) and K(j+2) are in
+//     flight. Buffers alternate by tile parity (the loop is unrolled by two), so every LDS
+//     offset is an immediate and the compiler sees that a load into one buffer cannot alias
+//     reads of the other.
 //   * Workgroup ids are remapped so the query tiles of one (b, h) run on the same XCD and
 //     share its L2 copy of K/V (dispatch hands consecutive workgroup ids to the 8 XCDs in turn).
 #include <type_traits>
@@ -103,7 +108,7 @@ template <> __device__ __forceinline__ void store4<f16_t>(f16_t* p, float a, flo
 constexpr int kFlashBM = 128;  // queries per workgroup
 constexpr int kFlashBN = 64;   // keys per tile
 
-// PV16: run P V in fp16 (P rounded to fp16, V converted bf16 -> fp16 as it is staged in LDS)
+// PV16: run P V in fp16 (P rounded to fp16, V converted bf16 -> fp16 in LDS after it lands)
 // instead of the input type. Used for bf16 inputs with an fp32 output, where bf16-rounded P
 // would be the dominant error of the result.
 template <typename T, int D, typename OutT, bool PV16>
@@ -112,17 +117,29 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   typedef typename std::conditional<PV16, f16_t, T>::type TV;  // type of V and P in P V
   typedef typename Mfma<TV>::vec vecv;
   constexpr int BN = kFlashBN;
-  constexpr int LDK = D + 8;           // K row stride in LDS, elements (16-byte pad)
-  constexpr int LDV = D + 32;          // V row stride: 64-byte pad. A row is then 16 dwords
-                                       // (mod 64) on from the last, and the transposed read of
-                                       // two 16-lane groups (4 rows x 2 x 32 bytes) hits 64
-                                       // distinct banks
-  constexpr int DC = D / 16;           // 16-wide d chunks of the QK^T contraction
-  constexpr int DB = D / 32;           // 32-row d blocks of O^T
-  constexpr int VPR = D / 8;           // 16-byte vectors per K/V row
-  constexpr int LOADS = BN * VPR / 256;
-  __shared__ __attribute__((aligned(16))) T Ks[2][BN * LDK];  // double-buffered tiles
-  __shared__ __attribute__((aligned(16))) TV Vs[2][BN * LDV];
+  constexpr int ROWB = D * 2;              // bytes per K/V row in LDS (no padding)
+  constexpr int GPR = D / 8;               // 16-byte granules per row
+  constexpr int RP256 = 256 / ROWB;        // rows per 256 bytes (one pass over the 64 banks)
+  constexpr int TILE = BN * ROWB;          // bytes per K or V tile
+  constexpr int CHUNKS = TILE / 1024;      // 1 KB pieces a wavefront's direct load fills
+  constexpr int CPW = CHUNKS / 4;          // ... per wavefront and tile
+  constexpr int RPC = 1024 / ROWB;         // rows per piece
+  constexpr int DC = D / 16;               // 16-wide d chunks of the QK^T contraction
+  constexpr int DB = D / 32;               // 32-row d blocks of O^T
+  static_assert(CPW >= 1, "tile too small for four wavefronts");
+  // Tiles land in LDS straight from global memory (buffer_load ... lds: 16 bytes per lane,
+  // a wavefront fills 1 KB of consecutive bytes per instruction), so rows cannot be padded.
+  // Instead the 16-byte granules of a row are XOR-swizzled: granule g of row r sits at
+  // position g ^ sk(r) (K) or g ^ sv(r) (V), chosen so that the K reads (16 rows, one granule
+  // each) and the transposed V reads (4 rows x 4 granules per half-wavefront) hit distinct
+  // banks. The loading lane picks the global granule that belongs at its LDS position.
+  // four separate LDS objects (not one array of buffers): the compiler then sees that a
+  // direct load into one buffer cannot alias reads of another and adds no wait for it
+  __shared__ __attribute__((aligned(1024))) unsigned char Ks0[TILE], Ks1[TILE], Vs0[TILE], Vs1[TILE];
+  unsigned char* const Ks[2] = {Ks0, Ks1};
+  unsigned char* const Vs[2] = {Vs0, Vs1};
+  auto sk = [](int r) { return (r / RP256) % GPR; };
+  auto sv = [](int r) { return 4 * ((r / RP256) % (GPR / 4)); };
 
   // workgroup -> (query tile, head, batch element); tiles of one head stay on one XCD
   const int nb = gridDim.x, bid = blockIdx.x;
@@ -160,7 +177,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
     }
     // Wait for these loads here, on every path. Otherwise the compiler may still count them as
     // outstanding at the head of the tile loop and wait there for all loads -- including the
-    // next tile's, issued one step earlier to hide their latency.
+    // next tiles', issued one step earlier to hide their latency.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
 
@@ -172,120 +189,148 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   const int key_end = a.full_cap ? ks.visit : row_limit(a.mask, a.block, q_last + shift, ks.len) + 1;
   const int key_full = row_limit(a.mask, a.block, q_first + shift, ks.len) + 1;
   const int my_lim = row_limit(a.mask, a.block, my_q + shift, ks.len);  // last key this row sees
-  const int full_end = min(key_end, (key_full / BN) * BN);
+  const int n_tiles = (key_end + BN - 1) / BN;
+  const int n_full = min(key_end, (key_full / BN) * BN) / BN;
 
   const int64_t rstride = (int64_t)a.Hkv * D;
   const T* kbase = (const T*)a.k + ks.base_row * rstride + (int64_t)g * D;
   const T* vbase = (const T*)a.v + ks.base_row * rstride + (int64_t)g * D;
-
-  uint4 kr[LOADS], vr[LOADS];
-  // Tile loads are buffer loads: a per-tile resource (uniform base = the tile's first row,
-  // size = its rows that exist) plus a loop-invariant 32-bit lane offset. Rows past the end of
-  // the visited range fall outside the resource and read as zero, so no load is branched,
-  // predicated or followed by a zero fill, and no per-load address arithmetic is needed.
-  uint32_t ld_off[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int idx = tid + 256 * i;
-    ld_off[i] = (uint32_t)(((idx / VPR) * rstride + 8 * (idx % VPR)) * sizeof(T));
-  }
   const int row_bytes = (int)(rstride * sizeof(T));
-  auto load_tile = [&](int tile) {
+
+  // Direct loads: piece c = wave * CPW + i of a tile covers rows [c * RPC, +RPC); lane L fills
+  // LDS bytes [c * 1024 + 16 L, +16), i.e. row c * RPC + L / GPR at position L % GPR, and so
+  // loads global granule (L % GPR) ^ swizzle(row). Offsets are loop-invariant; the per-tile
+  // resource (base = the tile's first row, size = its rows that exist) turns rows past the
+  // visited range into zeros.
+  uint32_t koff[CPW], voff[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int r = (wave * CPW + i) * RPC + lane / GPR, p = lane % GPR;
+    koff[i] = (uint32_t)(r * row_bytes + 16 * (p ^ sk(r)));
+    voff[i] = (uint32_t)(r * row_bytes + 16 * (p ^ sv(r)));
+  }
+  auto dma = [&](const T* base, int tile, unsigned char* dst, const uint32_t* off) {
     const int rows = min(ks.visit - tile, BN);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + (int64_t)tile * rstride), (short)0, rows * row_bytes, kBufferRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + (int64_t)tile * rstride), (short)0, rows * row_bytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (int64_t)tile * rstride), (short)0, rows * row_bytes, kBufferRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)ld_off[i], 0, 0);
-      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)ld_off[i], 0, 0);
-      __builtin_memcpy(&kr[i], &a, 16);
-      __builtin_memcpy(&vr[i], &c, 16);
-    }
+    for (int i = 0; i < CPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(dst + (wave * CPW + i) * 1024), 16,
+          (int)off[i], 0, 0, 0);
   };
-  auto store_tile = [&](int buf) {
+  // PV16: this thread converts, in place, the V granules its own direct loads wrote (its loads
+  // are complete once its vmcnt drains; the workgroup barrier then publishes the result)
+  auto convert_v = [&](unsigned char* dst) {
+    if constexpr (PV16) {
+      typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 h8;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int idx = tid + 256 * i;
-      const int key = idx / VPR, c8 = idx % VPR;
-      *(uint4*)&Ks[buf][key * LDK + 8 * c8] = kr[i];
-      if constexpr (PV16 && !std::is_same<T, f16_t>::value) {
-        const T* e = (const T*)&vr[i];
-        typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 h8;
-        h8 hv;
+      for (int i = 0; i < CPW; ++i) {
+        unsigned char* pp = dst + (wave * CPW + i) * 1024 + 16 * lane;
+        const bf16x8 x = *(const bf16x8*)pp;
+        h8 y;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) hv[k] = (f16_t)(float)e[k];
-        *(h8*)&Vs[buf][key * LDV + 8 * c8] = hv;
-      } else {
-        *(uint4*)&Vs[buf][key * LDV + 8 * c8] = vr[i];
+        for (int k = 0; k < 8; ++k) y[k] = (f16_t)(float)x[k];
+        *(h8*)pp = y;
       }
     }
   };
 
-  // transposed V reads: row and column offsets of this lane's 8-byte chunk (see the PV step)
+  // LDS read addresses. K (A operand of S^T): row sb*32 + l32, granule 2cc + hi -> position
+  // (2cc + hi) ^ sk(row); sk is the same for sb = 0, 1. V^T (transposed reads, see the PV
+  // step): row 16kc + 4hi + (lane%16)/4 (+8), column 32db + tr_col; the swizzle sv of these
+  // rows depends on the lane only.
+  const int swk = sk(l32);
+  uint32_t kaddr[DC];
+#pragma unroll
+  for (int cc = 0; cc < DC; ++cc) kaddr[cc] = l32 * ROWB + 16 * ((2 * cc + hi) ^ swk);
   const int tr_row = (lane & 15) >> 2;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vrow = 4 * hi + tr_row;
+  const int swv = sv(vrow);
+  uint32_t vaddr[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    vaddr[db] = vrow * ROWB + 16 * ((4 * db + tr_col / 8) ^ swv) + 2 * (tr_col % 8);
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
   float m = -INFINITY, lsum = 0.f;
   const float c = a.scale_log2;
+  f32x16 sacc[2][2];  // S^T of the current and the next tile (ping-pong by tile parity)
 
-  // One 64-key tile held in LDS buffer `buf`: S^T = K Q^T, online softmax, O^T += V^T P^T;
-  // meanwhile the next tile (already in registers) goes to the other buffer and the one after
-  // it is fetched from HBM -- one workgroup barrier per tile.
-  // MASKED selects the variant with the per-score visibility test; the two variants run in
-  // separate loops so no branch sits between the S^T products and their use.
-  auto step = [&](int tile, int buf, auto masked) {
-    constexpr bool MASKED = decltype(masked)::value;
-    const T* Kt = Ks[buf];
-    const TV* Vt = Vs[buf];
-
-    // s[sb][4i+j] = score(key tile+32sb+8i+4hi+j, query my_q)
-    f32x16 s[2];
-    __builtin_amdgcn_s_setprio(1);  // matrix-core phase: issue ahead of softmax waves
+  // S^T = K Q^T for the tile in K buffer kb: s[sb][4i+j] = score(key 32sb+8i+4hi+j, my_q)
+  auto qk = [&](int kb, f32x16* s) {
+    const unsigned char* Kt = Ks[kb];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       s[sb] = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < DC; ++cc) {
-        const vec ka = *(const vec*)&Kt[(sb * 32 + l32) * LDK + 16 * cc + 8 * hi];
+        const vec ka = *(const vec*)(Kt + sb * 32 * ROWB + kaddr[cc]);
         s[sb] = Mfma<T>::mma(ka, qreg[cc], s[sb]);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
-    float sv[2][16];
+  };
+
+  // One tile j (parity P): V of tile j is in Vs[P], K of tile j + 1 in Ks[P ^ 1]. Issue the
+  // direct loads of V(j+1) -> Vs[P^1] and K(j+2) -> Ks[P] (both buffers were last read before
+  // the previous barrier), compute S^T of tile j + 1 while the softmax of tile j runs, then
+  // O^T += V^T P^T, wait for this tile's loads and pass the workgroup barrier.
+  auto step = [&](int j, auto parity) {
+    constexpr int P = decltype(parity)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    const int tile = j * BN;
+    const bool has_next = j + 1 < n_tiles;
+    if (has_next) dma(vbase, tile + BN, Vs[P ^ 1], voff);
+    if (j + 2 < n_tiles) dma(kbase, tile + 2 * BN, Ks[P], koff);
+
+    f32x16* s = sacc[P];
+    float sv_[2][16];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = tile + 32 * sb + 8 * (r >> 2) + 4 * hi + (r & 3);
-        sv[sb][r] = (!MASKED || key <= my_lim) ? s[sb][r] : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r) sv_[sb][r] = s[sb][r];
+    if (j >= n_full) {  // diagonal tiles only (uniform branch)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = tile + 32 * sb + 8 * (r >> 2) + 4 * hi + (r & 3);
+          sv_[sb][r] = key <= my_lim ? sv_[sb][r] : -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv[sb][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sv_[sb][r]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // max with lane ^ 32
+    }
     // (mt - m) is NaN when both are -inf (a row with nothing visible yet): no move
     const bool grow = (mt - m) * c > kRescaleLog2;
     const float m_new = grow ? mt : m;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2((m - m_use) * c);  // exactly 1 while the reference stays
     const float mc = m_use * c;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sv[sb][r] = fast_exp2(fmaf(sv[sb][r], c, -mc));
     m = m_new;
     if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
 
+    // One block from here to the barrier: S^T of the next tile on the matrix cores while this
+    // tile's exponentials run on the vector ALUs, then O^T += V^T P^T. (The next tile's S^T is
+    // computed even past the last tile, from whatever the buffer holds, and unused then: a
+    // branch would split the block.)
+    qk(P ^ 1, sacc[P ^ 1]);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv_[sb][r] = fast_exp2(fmaf(sv_[sb][r], c, -mc));
     // P^T as B operands, one per 16-key chunk: k slot jj of lane half hi holds
     // key 4hi+jj (jj < 4) or 8+4hi+(jj-4) (jj >= 4) of the chunk. The row sum adds the
     // rounded values, the weights the product actually applies.
@@ -295,11 +340,13 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
     for (int kc = 0; kc < 4; ++kc) {
       const int sb = kc >> 1, r0 = 8 * (kc & 1);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) pb[kc][jj] = (TV)sv[sb][r0 + jj];
+      for (int jj = 0; jj < 8; ++jj) pb[kc][jj] = (TV)sv_[sb][r0 + jj];
       psum = sum8(pb[kc], psum);
     }
     lsum = lsum * alpha + psum;
+
     __builtin_amdgcn_s_setprio(1);
+    const unsigned char* Vt = Vs[P];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
@@ -308,32 +355,54 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
         // 16-lane group points at V[key0 + k/4][d0 + 4(k%4)], and lane i receives
         // V[key0 + t][d0 + i], t = 0..3 -- four keys of one d column. The keys are the MFMA
         // k slots 0..3 (keys 4hi+t of the chunk) and 4..7 (keys 8+4hi+t), the order P holds.
-        const TV* vp = Vt + (16 * kc + 4 * hi + tr_row) * LDV + 32 * db + tr_col;
+        const unsigned char* vp = Vt + 16 * kc * ROWB + vaddr[db];
         const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * LDV));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * ROWB));
         vecv va;
         __builtin_memcpy(&va, &x0, 8);
         __builtin_memcpy((char*)&va + 8, &x1, 8);
         o[db] = Mfma<TV>::mma(va, pb[kc], o[db]);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
-    if (tile + BN < key_end) {
-      store_tile(buf ^ 1);  // nobody reads that buffer: every wave passed the last barrier
-      if (tile + 2 * BN < key_end) load_tile(tile + 2 * BN);
+    // order within the block: each K read + S^T MFMA followed by softmax work, then the
+    // transposed V reads and P V MFMAs
+#pragma unroll
+    for (int i = 0; i < 2 * DC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read (K)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA (S^T)
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // vector ALU (softmax)
     }
+    // transposed V reads run three MFMAs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DB - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA (P V)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed V reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this thread's direct loads have landed
+    if (has_next) convert_v(Vs[P ^ 1]);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (key_end > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (BN < key_end) load_tile(BN);
+  if (n_tiles > 0) {
+    dma(kbase, 0, Ks[0], koff);
+    dma(vbase, 0, Vs[0], voff);
+    if (n_tiles > 1) dma(kbase, BN, Ks[1], koff);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    convert_v(Vs[0]);
     __syncthreads();
+    qk(0, sacc[0]);
+    __syncthreads();  // every wave has read Ks[0] before tile 0's step refills it
   }
-  int tile = 0, buf = 0;
-  for (; tile < full_end; tile += BN, buf ^= 1) step(tile, buf, std::false_type{});
-  for (; tile < key_end; tile += BN, buf ^= 1) step(tile, buf, std::true_type{});
+  int j = 0;
+  for (; j + 2 <= n_tiles; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    step(j + 1, std::integral_constant<int, 1>{});
+  }
+  if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
 
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
