@@ -49,7 +49,23 @@ def parse_args():
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--only", default="", help="profiling aid: run only this part "
                     "(decode | ring | multiuser | ragged | sweep | write)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="counter-profiling aid: finish with one plain device copy of 256 MiB "
+                    "(fresh buffers), whose FETCH_SIZE / WRITE_SIZE readings scale the "
+                    "counters of the other kernels in the same profile")
     return ap.parse_args()
+
+
+def copy_calibration(torch, dev):
+    """One torch device-to-device copy of exactly 256 MiB between fresh buffers: a kernel whose
+    HBM traffic is known (256 MiB read + 256 MiB written)."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
 
 
 # ----------------------------------------------------------------------------------------
@@ -123,6 +139,16 @@ class DecodeJob:
         self.decode_launch_bytes = [2 * (T + i + 1) * W.Hkv * W.D * ELEM + 2 * W.Hq * W.D * ELEM
                                     for i in range(W.steps)]
 
+    def run_steps(self):
+        """The fused decode steps alone, from the cursor at the end of the prefill (the cache
+        prefix is already in place; the steps rewrite their rows with the same values)."""
+        skv, W = self.skv, self.W
+        self.cursor.fill_(W.prompt)  # a fill kernel, safe to record in a graph
+        for i in range(W.steps):
+            skv.attn_decode_step(self.q_steps[i], self.k_steps[i], self.v_steps[i], self.kc, self.vc,
+                                 self.cursor, self.out[i], kv_len_out=self.kv_len,
+                                 max_seqlen_kv=self.max_kv, workspace=self.ws)
+
     def run(self, events=None):
         skv, W = self.skv, self.W
         self.cursor.zero_()  # a fill kernel, not a memset: safe to record in a graph
@@ -178,8 +204,28 @@ def bench_decode(torch, skv, SI, dev, args, fused=True):
     wall = (time.perf_counter() - t0) / args.steps
     gpu_ms = e0.elapsed_time(e1) / args.steps
 
-    # per-launch duration of the decode attention kernel: events around each launch, with the
-    # whole job enqueued behind a GPU-side sleep so host launch gaps do not enter the pairs
+    # per-launch duration of the decode attention kernel. Fused job: a graph of the 1024 steps
+    # alone, replayed and timed with one event pair -- back-to-back launches with nothing in
+    # between, as a kernel-trace profile times them. Both jobs: events around each launch
+    # (behind a GPU-side sleep, so host launch gaps do not enter) for the first / last step,
+    # and for the unfused job's attention launch, which sits between two other kernels.
+    steps_ms = None
+    if fused:
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            job.run_steps()
+        for _ in range(2):
+            g2.replay()
+        torch.cuda.synchronize()
+        reps = max(args.steps, 3)
+        c0, c1 = event_pair(torch)
+        c0.record()
+        for _ in range(reps):
+            g2.replay()
+        c1.record()
+        c1.synchronize()
+        steps_ms = c0.elapsed_time(c1) / (reps * job.W.steps)
+        del g2
     events = [event_pair(torch) for _ in range(job.W.steps)]
     t_host = time.perf_counter()
     job.run(events)  # host time to enqueue one job with its events
@@ -198,7 +244,7 @@ def bench_decode(torch, skv, SI, dev, args, fused=True):
         torch.cuda.synchronize()
         durations.append([a.elapsed_time(b) for a, b in events])
     per_launch = [statistics.median(d[i] for d in durations) for i in range(job.W.steps)]
-    mean_ms = sum(per_launch) / len(per_launch)
+    mean_ms = steps_ms if steps_ms is not None else sum(per_launch) / len(per_launch)
     mean_bytes = sum(job.decode_launch_bytes) / len(job.decode_launch_bytes)
     achieved = mean_bytes / (mean_ms * 1e-3) / 1e9
     return {
@@ -489,6 +535,8 @@ def main():
         line["rows"] = rows
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(SI, args.dtype)
+    if args.copy_calibration:
+        line["copy_calibration_bytes"] = copy_calibration(torch, dev)
     print(json.dumps(line))
 
 
