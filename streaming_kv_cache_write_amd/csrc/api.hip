@@ -149,7 +149,8 @@ skv_status kv_write_indexed(void* k_cache, void* v_cache, const void* k_src, con
   if (!index_dev && (start < 0 || start + n > cap))
     return fail(SKV_ERR_RANGE, "rows [%lld, %lld) outside the cache of %d rows", (long long)start,
                 (long long)(start + n), cap);
-  if ((int64_t)B * n > 0x7fffffff) return fail(SKV_ERR_SHAPE, "B*n too large");
+  if ((int64_t)B * n > 0x7fffffff || (int64_t)n * (row_bytes / 16) > 0x7fffffff)
+    return fail(SKV_ERR_SHAPE, "B*n or n*Hkv*D too large");
   if (B == 0 || n == 0) return ok();
   return hip_status(launch_write_indexed(k_src, v_src, k_cache, v_cache, index_dev, start, B, n,
                                          cap, (int)(row_bytes / 16), err_dev, (hipStream_t)stream),
@@ -182,6 +183,7 @@ skv_status kv_ring_create(skv_ring** out, void* k_store, void* v_store, void* me
     return fail(SKV_ERR_SHAPE, "ring too large");
   const int64_t row_bytes = (int64_t)Hkv * D * elem_bytes(dtype);
   if (row_bytes % 16) return fail(SKV_ERR_ALIGN, "row bytes not a multiple of 16");
+  if ((int64_t)chunk * (row_bytes / 16) > 0x7fffffff) return fail(SKV_ERR_SHAPE, "chunk too large");
   if (!aligned16(k_store) || !aligned16(v_store) || ((uintptr_t)meta_dev & 3))
     return fail(SKV_ERR_ALIGN, "misaligned ring storage or metadata");
   skv_ring* r = (skv_ring*)malloc(sizeof(skv_ring));

@@ -7,55 +7,56 @@
 // policy for streaming attention" (proposed boundary: fixed slots, reservation separate from
 // writes, pinned sink, device-resident slot metadata).
 //
-// A cache row (one token, all KV heads) is Hkv*D elements, contiguous: 0.5-10 KiB. Each
-// workgroup moves one source row of one tensor with 16-byte loads/stores; the grid is
-// (rows, tensors, chunks of 1024 vectors), so no per-element division is needed and every
-// wavefront issues fully coalesced 1 KiB accesses. The kernels are HBM-bound: each byte is
-// read once and written once.
+// A cache row (one token, all KV heads) is Hkv*D elements, contiguous: 0.5-10 KiB. The
+// source block of one batch element, [n, Hkv, D], is contiguous too, so each workgroup moves
+// an 8 KiB span of it (256 threads x 2 vectors of 16 bytes, both loads issued before the first
+// store) whatever the row size; each vector finds its destination row from its position
+// (longer spans per workgroup measured slower: 32 KiB spans halved the slab write rate). For
+// the ring the destination of a batch element's chunk is also one contiguous span (its slot),
+// so that write is a plain span copy with the slot read once per workgroup. The kernels are
+// HBM-bound: each byte is read once and written once.
 #include "common.h"
 
 namespace skv {
 
-constexpr int kCopyUnroll = 4;
-
-// Copy source row `row` (of n rows per batch element) to destination row `dst_row` of batch
-// element b. Vectors [blockIdx.z*blockDim*U, ...) of the row are handled by this block.
-__device__ __forceinline__ void copy_row(const uint4* __restrict__ src_, uint4* __restrict__ dst_,
-                                         int vpr) {
-  const i32x4* src = (const i32x4*)src_;  // native vector type for the nontemporal builtin
-  i32x4* dst = (i32x4*)dst_;
-  const int v0 = blockIdx.z * blockDim.x * kCopyUnroll + threadIdx.x;
-  i32x4 r[kCopyUnroll];
-#pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    int v = v0 + u * blockDim.x;
-    if (v < vpr) r[u] = __builtin_nontemporal_load(src + v);
-  }
-#pragma unroll
-  for (int u = 0; u < kCopyUnroll; ++u) {
-    int v = v0 + u * blockDim.x;
-    if (v < vpr) dst[v] = r[u];
-  }
-}
+constexpr int kCopyThreads = 256;
+constexpr int kCopyPer = 2;                           // 16-byte vectors per thread
+constexpr int kCopySpan = kCopyThreads * kCopyPer;    // vectors per workgroup (8 KiB)
 
 // index_copy along dim 1: cache[b, index[t]] = src[b, t] (index == nullptr: start + t).
-__global__ void __launch_bounds__(256)
-k_write_indexed(const uint4* __restrict__ k_src, const uint4* __restrict__ v_src,
-                uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+// Grid: (B * spans per batch element, tensors). Vector i of batch element b's source block is
+// row t = i / vpr, column i % vpr; it goes to row index[t] of b's cache.
+__global__ void __launch_bounds__(kCopyThreads)
+k_write_indexed(const i32x4* __restrict__ k_src, const i32x4* __restrict__ v_src,
+                i32x4* __restrict__ k_cache, i32x4* __restrict__ v_cache,
                 const int64_t* __restrict__ index, int64_t start, int n, int cap, int vpr,
-                int32_t* err) {
-  const int row = blockIdx.x;  // b * n + t
-  const int b = row / n;
-  const int t = row - b * n;
+                int spans, int32_t* err) {
+  const int b = blockIdx.x / spans;
+  const int span = blockIdx.x - b * spans;
   const bool is_v = blockIdx.y != 0;
-  const int64_t dst_row = index ? index[t] : start + t;
-  if (dst_row < 0 || dst_row >= cap) {
-    if (!is_v && blockIdx.z == 0 && threadIdx.x == 0) report(err, SKV_DEV_INDEX_RANGE);
-    return;
+  const int nv = n * vpr;  // vectors per batch element (host-checked to fit an int)
+  const i32x4* src = (is_v ? v_src : k_src) + (int64_t)b * nv;
+  i32x4* cache = (is_v ? v_cache : k_cache) + (int64_t)b * cap * vpr;
+  const int i0 = span * kCopySpan + threadIdx.x;
+  i32x4 r[kCopyPer];
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const int i = i0 + u * kCopyThreads;
+    if (i < nv) r[u] = __builtin_nontemporal_load(src + i);
   }
-  const uint4* src = (is_v ? v_src : k_src) + (int64_t)row * vpr;
-  uint4* dst = (is_v ? v_cache : k_cache) + ((int64_t)b * cap + dst_row) * vpr;
-  copy_row(src, dst, vpr);
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const int i = i0 + u * kCopyThreads;
+    if (i >= nv) continue;
+    const int t = i / vpr;
+    const int col = i - t * vpr;
+    const int64_t dst_row = index ? index[t] : start + t;
+    if (dst_row < 0 || dst_row >= cap) {
+      if (!is_v && col == 0) report(err, SKV_DEV_INDEX_RANGE);
+      continue;
+    }
+    cache[dst_row * vpr + col] = r[u];
+  }
 }
 
 // Device cursor: index[t] = c + t, kv_len[b] = c + n, cursor = c + n (if it fits).
@@ -119,15 +120,16 @@ __global__ void k_ring_reserve(int32_t* meta, int B, const uint8_t* mask, int n_
   }
 }
 
-// Write the current chunk [B, C, Hkv, D] into its reserved slot. Block (0,0,0) also commits
-// the retained-token count at the first write after a reserve; every other block only reads
-// slot[], which no block of this launch modifies.
-__global__ void __launch_bounds__(256)
-k_ring_write(const uint4* __restrict__ k_src, const uint4* __restrict__ v_src,
-             uint4* __restrict__ k_store, uint4* __restrict__ v_store, int32_t* meta, int B,
-             const uint8_t* mask, int C, int n_slots, int vpr, int32_t* err) {
+// Write the current chunk [B, C, Hkv, D] into its reserved slot. Block (0,0) also commits the
+// retained-token count at the first write after a reserve; every other block only reads
+// slot[], which no block of this launch modifies. Grid: (B * spans per chunk, tensors); a
+// batch element's chunk and its slot's rows are both contiguous, so this is a span copy.
+__global__ void __launch_bounds__(kCopyThreads)
+k_ring_write(const i32x4* __restrict__ k_src, const i32x4* __restrict__ v_src,
+             i32x4* __restrict__ k_store, i32x4* __restrict__ v_store, int32_t* meta, int B,
+             const uint8_t* mask, int C, int n_slots, int vpr, int spans, int32_t* err) {
   RingMeta m = ring_meta(meta, B);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
     for (int b = threadIdx.x; b < B; b += blockDim.x) {
       if (!selected(mask, b)) continue;
       if (m.slot[b] < 0) {
@@ -141,38 +143,42 @@ k_ring_write(const uint4* __restrict__ k_src, const uint4* __restrict__ v_src,
       }
     }
   }
-  const int row = blockIdx.x;  // b * C + t
-  const int b = row / C;
-  const int t = row - b * C;
+  const int b = blockIdx.x / spans;
+  const int span = blockIdx.x - b * spans;
   if (!selected(mask, b)) return;
   const int s = m.slot[b];
   if (s < 0 || s >= n_slots) return;  // unreserved (reported by block 0) or corrupt metadata
   const bool is_v = blockIdx.y != 0;
-  const uint4* src = (is_v ? v_src : k_src) + (int64_t)row * vpr;
-  uint4* dst = (is_v ? v_store : k_store) + ((int64_t)b * n_slots * C + (int64_t)s * C + t) * vpr;
-  copy_row(src, dst, vpr);
+  const int nv = C * vpr;  // vectors per chunk (checked to fit an int when the ring was made)
+  const i32x4* src = (is_v ? v_src : k_src) + (int64_t)b * nv;
+  i32x4* dst = (is_v ? v_store : k_store) + ((int64_t)b * n_slots + s) * nv;
+  const int i0 = span * kCopySpan + threadIdx.x;
+  i32x4 r[kCopyPer];
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const int i = i0 + u * kCopyThreads;
+    if (i < nv) r[u] = __builtin_nontemporal_load(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const int i = i0 + u * kCopyThreads;
+    if (i < nv) dst[i] = r[u];
+  }
 }
 
 // ---------------------------------------------------------------------------------------
 // Host launchers (called by api.hip after argument validation)
 // ---------------------------------------------------------------------------------------
-static dim3 copy_block(int vpr) {
-  int threads = vpr >= 256 ? 256 : ((vpr + 63) / 64) * 64;
-  return dim3(threads);
-}
-
-static dim3 copy_grid(int rows, int tensors, int vpr, int threads) {
-  int per_block = threads * kCopyUnroll;
-  return dim3(rows, tensors, (vpr + per_block - 1) / per_block);
-}
+static int copy_spans(int64_t vectors) { return (int)((vectors + kCopySpan - 1) / kCopySpan); }
 
 hipError_t launch_write_indexed(const void* k_src, const void* v_src, void* k_cache, void* v_cache,
                                 const int64_t* index, int64_t start, int B, int n, int cap,
                                 int vpr, int32_t* err, hipStream_t s) {
-  dim3 blk = copy_block(vpr);
-  dim3 grd = copy_grid(B * n, v_cache ? 2 : 1, vpr, blk.x);
-  hipLaunchKernelGGL(k_write_indexed, grd, blk, 0, s, (const uint4*)k_src, (const uint4*)v_src,
-                     (uint4*)k_cache, (uint4*)v_cache, index, start, n, cap, vpr, err);
+  const int spans = copy_spans((int64_t)n * vpr);
+  dim3 grd((unsigned)((int64_t)B * spans), v_cache ? 2 : 1);
+  hipLaunchKernelGGL(k_write_indexed, grd, dim3(kCopyThreads), 0, s, (const i32x4*)k_src,
+                     (const i32x4*)v_src, (i32x4*)k_cache, (i32x4*)v_cache, index, start, n, cap,
+                     vpr, spans, err);
   return hipGetLastError();
 }
 
@@ -197,10 +203,11 @@ hipError_t launch_ring_reserve(int32_t* meta, int B, const uint8_t* mask, int n_
 hipError_t launch_ring_write(const void* k_src, const void* v_src, void* k_store, void* v_store,
                              int32_t* meta, int B, const uint8_t* mask, int C, int n_slots,
                              int vpr, int32_t* err, hipStream_t s) {
-  dim3 blk = copy_block(vpr);
-  dim3 grd = copy_grid(B * C, v_store ? 2 : 1, vpr, blk.x);
-  hipLaunchKernelGGL(k_ring_write, grd, blk, 0, s, (const uint4*)k_src, (const uint4*)v_src,
-                     (uint4*)k_store, (uint4*)v_store, meta, B, mask, C, n_slots, vpr, err);
+  const int spans = copy_spans((int64_t)C * vpr);
+  dim3 grd((unsigned)((int64_t)B * spans), v_store ? 2 : 1);
+  hipLaunchKernelGGL(k_ring_write, grd, dim3(kCopyThreads), 0, s, (const i32x4*)k_src,
+                     (const i32x4*)v_src, (i32x4*)k_store, (i32x4*)v_store, meta, B, mask, C,
+                     n_slots, vpr, spans, err);
   return hipGetLastError();
 }
 
