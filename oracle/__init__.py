@@ -24,8 +24,11 @@ Modules:
   (two-pass, max-subtracted, fp64), a scalar brute-force twin, the key-set
   rules (masks, active prefix, packed segments, GQA head map).
 * ``oracle.cache`` -- slab writes (explicit row loop), the ring as a physical
-  slot simulation that picks slots by search, and a chronological history
-  that defines what the ring must retain.
+  slot simulation that picks slots by search, a chronological history that
+  defines what the ring must retain, and the chronological buffer with the
+  roll-left copy that the ring replaces (the comparison arm).
+* ``oracle.ragged`` -- packing of ragged K/V (each branch's valid rows
+  concatenated) and its prefix-sum metadata.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, brute force, library routines (torch CPU fp64 SDPA) and the values the

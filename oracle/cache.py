@@ -19,7 +19,7 @@ slot is reserved separately from its writes, so the repeated denoising writes
 of one chunk all land in the same slot. Reset forgets the contents. Cond and
 uncond branches keep independent state.
 
-Two independent formulations are kept, and the tests pin one to the other:
+Three independent formulations are kept, and the tests pin them to each other:
 
 * ``RingChronological`` -- the history of chunks since reset, in order; the
   retained set is the sink chunks followed by the newest chunks that fit.
@@ -27,6 +27,11 @@ Two independent formulations are kept, and the tests pin one to the other:
   slot, else the slot holding the oldest non-sink chunk, found by searching
   the slots' chunk ids (no closed-form slot formula). Reset empties every slot
   but leaves the stale rows in place.
+* ``RollingChronological`` -- the chronological buffer the page's current path
+  keeps (section current path: when a new chunk overflows the window, the
+  retained window is copied left by one chunk): rows in time order, the sink
+  chunks first, a full buffer moved left past the sink by one chunk (``roll_left``)
+  before the new chunk goes to its end.
 
 Readings taken where the page is silent:
 
@@ -198,3 +203,65 @@ class RingPhysical:
     def physical_prefix(self) -> np.ndarray:
         """Rows [0, valid_tokens) in physical slot order: what prefix attention reads."""
         return self.storage[:self.valid_tokens()]
+
+
+# ----------------------------------------------------------------------------------------
+# Chronological buffer with roll-left (the comparison arm)
+# ----------------------------------------------------------------------------------------
+
+def roll_left(store: np.ndarray, sink_rows: int, shift_rows: int, rows: int) -> np.ndarray:
+    """Move rows [sink_rows + shift_rows, rows) of store to [sink_rows, rows - shift_rows);
+    rows outside [sink_rows, rows - shift_rows) keep their contents (flashdreams issue #763,
+    section current path: the retained tokens are copied left by one chunk). Defined as a
+    copy of the moved block, so an overlap of source and destination does not matter."""
+    if not (0 <= sink_rows and 0 < shift_rows and sink_rows + shift_rows <= rows <= store.shape[0]):
+        raise ValueError(f"bad roll: sink {sink_rows}, shift {shift_rows}, rows {rows}")
+    out = store.copy()
+    out[sink_rows:rows - shift_rows] = store[sink_rows + shift_rows:rows].copy()
+    return out
+
+
+class RollingChronological:
+    """Chronological buffer of n_slots * C rows for one batch element, as the page's current
+    path keeps it. The chunk lifecycle matches the ring's (reserve, then one or more writes of
+    the same chunk, reset); only the placement differs: a chunk goes to the end of the filled
+    rows, and when the buffer is full the non-sink part first moves left by one chunk."""
+
+    def __init__(self, n_slots: int, sink: int, C: int, row_shape: tuple, dtype=np.float64):
+        if not (0 <= sink < n_slots):
+            raise ValueError("need 0 <= sink < n_slots")
+        self.n_slots, self.sink, self.C = n_slots, sink, C
+        self.rows = n_slots * C
+        self.store = np.zeros((self.rows,) + tuple(row_shape), dtype=dtype)
+        self.filled = 0       # rows holding retained tokens, a multiple of C
+        self.chunks = 0       # chunks since reset
+        self.open = False     # a reserved chunk awaits its first write
+        self.rolls = 0        # roll_left calls so far (the maintenance the ring avoids)
+
+    def reserve(self) -> None:
+        self.open = True
+
+    def write(self, chunk: np.ndarray) -> bool:
+        """First write after a reserve places a new chunk (rolling if full); later writes
+        replace the current chunk. Returns False when nothing was ever reserved since reset."""
+        if self.open:
+            if self.filled + self.C > self.rows:  # full: drop the oldest non-sink chunk
+                self.store = roll_left(self.store, self.sink * self.C, self.C, self.rows)
+                self.rolls += 1
+            else:
+                self.filled += self.C
+            self.chunks += 1
+            self.open = False
+        elif self.chunks == 0:
+            return False
+        self.store[self.filled - self.C:self.filled] = chunk
+        return True
+
+    def reset(self) -> None:
+        self.filled = 0
+        self.chunks = 0
+        self.open = False
+
+    def valid(self) -> np.ndarray:
+        """The retained rows, oldest to newest."""
+        return self.store[:self.filled]

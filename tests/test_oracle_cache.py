@@ -191,3 +191,68 @@ def test_planted_unpinned_sink_is_caught(monkeypatch):
     monkeypatch.setattr(Cc.RingPhysical, "_choose_slot", no_sink)
     with pytest.raises(AssertionError):
         run_layout(1, 3, 2, 1, attend=False)
+
+
+# ----------------------------------------------------------------------------------------
+# The chronological roll-left buffer (comparison arm), pinned to the chunk history
+# ----------------------------------------------------------------------------------------
+
+def run_rolling(sink, rolling, C, B):
+    """Drive the roll-left buffer and the chronological history through the same sequence
+    (repeated writes, a reset mid-sequence); compare the buffer's valid rows with the
+    retained chunks after every write. Returns the number of comparisons."""
+    n_slots = sink + rolling
+    Hkv, D = 1, 3
+    roll = [Cc.RollingChronological(n_slots, sink, C, (Hkv, D)) for _ in range(B)]
+    chron = [Cc.RingChronological(n_slots, sink) for _ in range(B)]
+    ops = ring_sequence(n_slots + 2 * rolling + 1, lambda c: 1 + (c % 3), 3)
+    n = 0
+    for op, seg, c, r in ops:
+        for b in range(B):
+            if op == "reserve":
+                roll[b].reserve()
+                chron[b].reserve()
+            elif op == "reset":
+                roll[b].reset()
+                chron[b].reset()
+            else:
+                chunk = rng.standard_normal((C, Hkv, D))
+                assert roll[b].write(chunk) == chron[b].write(chunk)
+                np.testing.assert_array_equal(roll[b].valid(), np.concatenate(chron[b].retained(), axis=0))
+                n += 1
+    return n
+
+
+@pytest.mark.parametrize("sink,rolling,C,B", LAYOUTS)
+def test_rolling_buffer_equals_chronological(sink, rolling, C, B):
+    assert run_rolling(sink, rolling, C, B) > 0
+
+
+def test_roll_left_fixture():
+    """Rows labelled by position: sink 2 rows, shift 3, 10 rows -> rows 5..9 move to 2..6,
+    rows 0, 1 stay, rows 7..9 keep their old contents."""
+    x = np.arange(10, dtype=np.float64)[:, None]
+    y = Cc.roll_left(x, 2, 3, 10)
+    np.testing.assert_array_equal(y[:, 0], [0, 1, 5, 6, 7, 8, 9, 7, 8, 9])
+    with pytest.raises(ValueError):
+        Cc.roll_left(x, 8, 3, 10)
+
+
+def test_rolling_counts_one_roll_per_new_chunk_once_full():
+    """7 slots, sink 1, 12 chunks with 4 writes each: rolls start at chunk 7 (the first that
+    does not fit) -> 5 rolls, 23400 rows moved per roll for C = 4680 (the f2 figure)."""
+    r = Cc.RollingChronological(7, 1, 2, (1,))
+    for c in range(12):
+        r.reserve()
+        for _ in range(4):
+            r.write(np.full((2, 1), float(c)))
+    assert r.rolls == 5
+    np.testing.assert_array_equal(r.valid()[:, 0], [0, 0, 6, 6, 7, 7, 8, 8, 9, 9, 10, 10, 11, 11])
+    assert (7 - 1 - 1) * 4680 == 23400
+
+
+def test_planted_roll_without_sink_is_caught(monkeypatch):
+    real = Cc.roll_left
+    monkeypatch.setattr(Cc, "roll_left", lambda s, sink, shift, rows: real(s, 0, shift, rows))
+    with pytest.raises(AssertionError):
+        run_rolling(1, 3, 2, 1)
