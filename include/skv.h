@@ -141,6 +141,42 @@ const int32_t* kv_ring_slot_dev(const skv_ring* ring);   /* slot[B], device */
 skv_status kv_ring_destroy(skv_ring* ring);
 
 /* ------------------------------------------------------------------------------------
+ * Roll-left of a chronological window: the comparison arm [FD, current path]
+ *
+ * The cache the ring replaces keeps rows in time order, sink first; when a new chunk
+ * overflows the window, the retained non-sink rows move left by one chunk, and the new chunk
+ * is then written at the end (kv_write_indexed at rows [rows - shift_rows, rows)).
+ * kv_roll_left moves rows [sink_rows + shift_rows, rows) of every batch element of
+ * k_store / v_store [B, rows, Hkv, D] to [sink_rows, rows - shift_rows), with memmove
+ * semantics (source and destination overlap): it enqueues copies of at most shift_rows rows
+ * in increasing row order on `stream`, each reading rows that no earlier copy writes. Rows
+ * [rows - shift_rows, rows) keep their old contents. v_store NULL: K only. Requires
+ * 0 <= sink_rows, 1 <= shift_rows, sink_rows + shift_rows <= rows (equality: nothing moves).
+ * ------------------------------------------------------------------------------------ */
+skv_status kv_roll_left(void* k_store, void* v_store, int B, int rows, int sink_rows,
+                        int shift_rows, int Hkv, int D, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Ragged K/V packing [TR, Description; Acceptance criteria]
+ *
+ * kv_ragged_metadata: cu_seqlens_out_dev[0] = 0 and cu[b+1] = cu[b] + lens_dev[b] (int32
+ * [B] in, int32 [B+1] out, device, one launch). A length outside [0, max_kv] counts as 0 and
+ * sets SKV_DEV_KV_LEN. The metadata depends only on the length layout, so it is prepared once
+ * per layout [TR, Description]; attention then takes cu_seqlens_kv with max_seqlen_kv = max_kv.
+ * kv_pack_ragged: for every b, rows [0, len_b) of k_padded / v_padded [B, max_kv, Hkv, D] go
+ * to rows [cu[b], cu[b] + len_b) of k_packed / v_packed [packed_rows, Hkv, D], where
+ * len_b = cu[b+1] - cu[b] (the key padding is at the end of each branch). A segment that
+ * does not fit (cu[b] < 0, len_b < 0 or > max_kv, cu[b+1] > packed_rows) is skipped and sets
+ * SKV_DEV_CU_SEQLENS. v_packed / v_padded NULL: K only. With packed_rows == 0 the packed
+ * pointers may be NULL: no row is written, and any non-empty segment sets SKV_DEV_CU_SEQLENS.
+ * ------------------------------------------------------------------------------------ */
+skv_status kv_ragged_metadata(const int32_t* lens_dev, int B, int max_kv, int32_t* cu_seqlens_out_dev,
+                              int32_t* err_dev, void* stream);
+skv_status kv_pack_ragged(void* k_packed, void* v_packed, const void* k_padded, const void* v_padded,
+                          const int32_t* cu_seqlens_dev, int B, int max_kv, int packed_rows, int Hkv,
+                          int D, int dtype, int32_t* err_dev, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Chunk attention over a KV cache [FS, Problem; Change] [TR, Description]
  *
  *     out[b, t, h, :] = sum_j softmax_j(scale * <q[b,t,h,:], k_j>) v_j

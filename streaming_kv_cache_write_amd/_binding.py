@@ -69,6 +69,9 @@ _SIGS = {
     "kv_ring_kv_len_dev": (_vp, [_vp]),
     "kv_ring_slot_dev": (_vp, [_vp]),
     "kv_ring_destroy": (_i, [_vp]),
+    "kv_roll_left": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "kv_ragged_metadata": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "kv_pack_ragged": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "attn_workspace_bytes": (_sz, [ctypes.POINTER(skv_attn_params)]),
     "attn_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, ctypes.POINTER(skv_attn_params), _vp]),
     "attn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -143,6 +146,50 @@ def kv_cursor_advance(cursor, n: int, cap: int, index_out, kv_len_out=None, err=
         _dev_tensor(err, "err", torch.int32)
     _check(lib.kv_cursor_advance(_ptr(cursor), int(n), int(cap), B, _ptr(index_out),
                                  _ptr(kv_len_out), _ptr(err), _stream(cursor.device)))
+
+
+def kv_roll_left(k_store, v_store, sink_rows: int, shift_rows: int):
+    """Move rows [sink_rows + shift_rows, rows) of k_store/v_store [B, rows, Hkv, D] to
+    [sink_rows, rows - shift_rows) (memmove semantics): the chronological window's roll-left."""
+    _dev_tensor(k_store, "k_store")
+    B, rows, Hkv, D = k_store.shape
+    if v_store is not None:
+        _dev_tensor(v_store, "v_store", k_store.dtype)
+    _check(lib.kv_roll_left(_ptr(k_store), _ptr(v_store), B, rows, int(sink_rows), int(shift_rows),
+                            Hkv, D, dtype_code(k_store.dtype), _stream(k_store.device)))
+
+
+def kv_ragged_metadata(lens, max_kv: int, cu_seqlens_out=None, err=None):
+    """cu_seqlens_kv [B+1] int32 (exclusive prefix sums of lens [B] int32), on the device."""
+    _dev_tensor(lens, "lens", torch.int32)
+    B = lens.numel()
+    if cu_seqlens_out is None:
+        cu_seqlens_out = torch.empty(B + 1, dtype=torch.int32, device=lens.device)
+    _dev_tensor(cu_seqlens_out, "cu_seqlens_out", torch.int32)
+    if cu_seqlens_out.numel() != B + 1:
+        raise ValueError("cu_seqlens_out must have B+1 entries")
+    if err is not None:
+        _dev_tensor(err, "err", torch.int32)
+    _check(lib.kv_ragged_metadata(_ptr(lens), B, int(max_kv), _ptr(cu_seqlens_out), _ptr(err),
+                                  _stream(lens.device)))
+    return cu_seqlens_out
+
+
+def kv_pack_ragged(k_padded, v_padded, cu_seqlens, k_packed, v_packed=None, err=None):
+    """Rows [0, len_b) of k_padded/v_padded [B, max_kv, Hkv, D] to rows [cu[b], cu[b+1]) of
+    k_packed/v_packed [packed_rows, Hkv, D], len_b = cu[b+1] - cu[b]."""
+    _dev_tensor(k_padded, "k_padded")
+    B, max_kv, Hkv, D = k_padded.shape
+    _dev_tensor(k_packed, "k_packed", k_padded.dtype)
+    if v_padded is not None:
+        _dev_tensor(v_padded, "v_padded", k_padded.dtype)
+        _dev_tensor(v_packed, "v_packed", k_padded.dtype)
+    _dev_tensor(cu_seqlens, "cu_seqlens", torch.int32)
+    if err is not None:
+        _dev_tensor(err, "err", torch.int32)
+    _check(lib.kv_pack_ragged(_ptr(k_packed), _ptr(v_packed), _ptr(k_padded), _ptr(v_padded),
+                              _ptr(cu_seqlens), B, max_kv, k_packed.shape[0], Hkv, D,
+                              dtype_code(k_padded.dtype), _ptr(err), _stream(k_padded.device)))
 
 
 class Ring:

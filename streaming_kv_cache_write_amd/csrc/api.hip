@@ -17,6 +17,10 @@ hipError_t launch_ring_reset(int32_t*, int, const uint8_t*, hipStream_t);
 hipError_t launch_ring_reserve(int32_t*, int, const uint8_t*, int, int, hipStream_t);
 hipError_t launch_ring_write(const void*, const void*, void*, void*, int32_t*, int, const uint8_t*,
                              int, int, int, int32_t*, hipStream_t);
+hipError_t launch_roll_left(void*, void*, int, int, int, int, int, hipStream_t);
+hipError_t launch_ragged_metadata(const int32_t*, int, int, int32_t*, int32_t*, hipStream_t);
+hipError_t launch_pack_ragged(const void*, const void*, void*, void*, const int32_t*, int, int, int,
+                              int, int32_t*, hipStream_t);
 hipError_t launch_attn_f32(const AttnArgs&, int, hipStream_t);
 hipError_t launch_attn_flash(const AttnArgs&, int, int, int, hipStream_t);
 hipError_t launch_attn_decode(const AttnArgs&, int, int, int, void*, int, hipStream_t);
@@ -231,6 +235,61 @@ const int32_t* kv_ring_slot_dev(const skv_ring* r) { return r ? r->meta + r->B :
 skv_status kv_ring_destroy(skv_ring* r) {
   free(r);
   return ok();
+}
+
+skv_status kv_roll_left(void* k_store, void* v_store, int B, int rows, int sink_rows,
+                        int shift_rows, int Hkv, int D, int dtype, void* stream) {
+  if (!k_store) return fail(SKV_ERR_NULL, "k_store must be non-NULL");
+  if (!elem_bytes(dtype)) return fail(SKV_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (B < 0 || rows < 1 || Hkv < 1 || D < 1) return fail(SKV_ERR_SHAPE, "bad sizes");
+  if (sink_rows < 0 || shift_rows < 1 || (int64_t)sink_rows + shift_rows > rows)
+    return fail(SKV_ERR_RANGE, "need 0 <= sink_rows, 1 <= shift_rows, sink_rows + shift_rows <= rows "
+                "(got %d, %d, %d)", sink_rows, shift_rows, rows);
+  const int64_t row_bytes = (int64_t)Hkv * D * elem_bytes(dtype);
+  if (row_bytes % 16) return fail(SKV_ERR_ALIGN, "row bytes not a multiple of 16");
+  if (!aligned16(k_store) || !aligned16(v_store)) return fail(SKV_ERR_ALIGN, "misaligned storage");
+  if ((int64_t)shift_rows * (row_bytes / 16) > 0x7fffffff) return fail(SKV_ERR_SHAPE, "shift too large");
+  if (B == 0 || sink_rows + shift_rows == rows) return ok();
+  return hip_status(launch_roll_left(k_store, v_store, B, rows, sink_rows, shift_rows,
+                                     (int)(row_bytes / 16), (hipStream_t)stream),
+                    "kv_roll_left launch");
+}
+
+skv_status kv_ragged_metadata(const int32_t* lens_dev, int B, int max_kv, int32_t* cu_seqlens_out_dev,
+                              int32_t* err_dev, void* stream) {
+  if (!lens_dev || !cu_seqlens_out_dev) return fail(SKV_ERR_NULL, "lens_dev and cu_seqlens_out_dev must be non-NULL");
+  if (B < 1 || max_kv < 0) return fail(SKV_ERR_SHAPE, "need B >= 1, max_kv >= 0");
+  if ((int64_t)B * max_kv > 0x7fffffff) return fail(SKV_ERR_SHAPE, "B*max_kv too large");
+  if (((uintptr_t)lens_dev & 3) || ((uintptr_t)cu_seqlens_out_dev & 3))
+    return fail(SKV_ERR_ALIGN, "misaligned lens / cu_seqlens");
+  return hip_status(launch_ragged_metadata(lens_dev, B, max_kv, cu_seqlens_out_dev, err_dev,
+                                           (hipStream_t)stream),
+                    "kv_ragged_metadata launch");
+}
+
+skv_status kv_pack_ragged(void* k_packed, void* v_packed, const void* k_padded, const void* v_padded,
+                          const int32_t* cu_seqlens_dev, int B, int max_kv, int packed_rows, int Hkv,
+                          int D, int dtype, int32_t* err_dev, void* stream) {
+  const bool no_rows = packed_rows == 0;  // packed buffers may then be NULL (nothing is written)
+  if (!k_padded || !cu_seqlens_dev || (!k_packed && !no_rows))
+    return fail(SKV_ERR_NULL, "k_packed, k_padded and cu_seqlens_dev must be non-NULL");
+  if (!no_rows && (v_packed == nullptr) != (v_padded == nullptr))
+    return fail(SKV_ERR_NULL, "v_packed and v_padded must both be given or both be NULL");
+  if (!elem_bytes(dtype)) return fail(SKV_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (B < 1 || max_kv < 0 || packed_rows < 0 || Hkv < 1 || D < 1)
+    return fail(SKV_ERR_SHAPE, "bad sizes B=%d max_kv=%d packed_rows=%d Hkv=%d D=%d", B, max_kv,
+                packed_rows, Hkv, D);
+  const int64_t row_bytes = (int64_t)Hkv * D * elem_bytes(dtype);
+  if (row_bytes % 16) return fail(SKV_ERR_ALIGN, "row bytes not a multiple of 16");
+  if (!aligned16(k_packed) || !aligned16(v_packed) || !aligned16(k_padded) || !aligned16(v_padded) ||
+      ((uintptr_t)cu_seqlens_dev & 3))
+    return fail(SKV_ERR_ALIGN, "misaligned buffers");
+  if ((int64_t)max_kv * (row_bytes / 16) > 0x7fffffff) return fail(SKV_ERR_SHAPE, "max_kv too large");
+  if (max_kv == 0) return ok();
+  return hip_status(launch_pack_ragged(k_padded, v_padded, k_packed, v_packed, cu_seqlens_dev, B,
+                                       max_kv, packed_rows, (int)(row_bytes / 16), err_dev,
+                                       (hipStream_t)stream),
+                    "kv_pack_ragged launch");
 }
 
 size_t attn_workspace_bytes(const skv_attn_params* p) {

@@ -167,6 +167,83 @@ k_ring_write(const i32x4* __restrict__ k_src, const i32x4* __restrict__ v_src,
 }
 
 // ---------------------------------------------------------------------------------------
+// Chronological window roll-left (comparison arm) and ragged K/V packing
+// ---------------------------------------------------------------------------------------
+
+// Block move per batch element: vectors [0, nv) of src + b * src_stride go to dst + b *
+// dst_stride; the caller guarantees that source and destination do not overlap.
+__global__ void __launch_bounds__(kCopyThreads)
+k_move_block(const i32x4* __restrict__ k_src, i32x4* __restrict__ k_dst, const i32x4* v_src,
+             i32x4* v_dst, int64_t src_stride, int64_t dst_stride, int nv, int spans) {
+  const int b = blockIdx.x / spans;
+  const int span = blockIdx.x - b * spans;
+  const bool is_v = blockIdx.y != 0;
+  const i32x4* src = (is_v ? v_src : k_src) + (int64_t)b * src_stride;
+  i32x4* dst = (is_v ? v_dst : k_dst) + (int64_t)b * dst_stride;
+  const int i0 = span * kCopySpan + threadIdx.x;
+  i32x4 r[kCopyPer];
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const int i = i0 + u * kCopyThreads;
+    if (i < nv) r[u] = __builtin_nontemporal_load(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const int i = i0 + u * kCopyThreads;
+    if (i < nv) dst[i] = r[u];
+  }
+}
+
+// cu[0] = 0, cu[b+1] = cu[b] + len_b, lengths outside [0, max_kv] counted as 0 (flagged).
+__global__ void k_ragged_metadata(const int32_t* lens, int B, int max_kv, int32_t* cu, int32_t* err) {
+  if (threadIdx.x != 0) return;
+  int64_t acc = 0;
+  cu[0] = 0;
+  bool bad = false;
+  for (int b = 0; b < B; ++b) {
+    int l = lens[b];
+    if (l < 0 || l > max_kv) {
+      bad = true;
+      l = 0;
+    }
+    acc += l;
+    cu[b + 1] = (int32_t)acc;
+  }
+  if (bad) report(err, SKV_DEV_KV_LEN);
+}
+
+// Packing: vector i of batch element b's padded block is row t = i / vpr; rows t < len_b go
+// to packed row cu[b] + t. Grid: (B * spans over max_kv rows, tensors).
+__global__ void __launch_bounds__(kCopyThreads)
+k_pack_ragged(const i32x4* __restrict__ k_pad, const i32x4* __restrict__ v_pad,
+              i32x4* __restrict__ k_pack, i32x4* __restrict__ v_pack, const int32_t* cu, int max_kv,
+              int packed_rows, int vpr, int spans, int32_t* err) {
+  const int b = blockIdx.x / spans;
+  const int span = blockIdx.x - b * spans;
+  const bool is_v = blockIdx.y != 0;
+  const int lo = cu[b], len = cu[b + 1] - lo;
+  if (lo < 0 || len < 0 || len > max_kv || (int64_t)lo + len > packed_rows) {
+    if (!is_v && span == 0 && threadIdx.x == 0) report(err, SKV_DEV_CU_SEQLENS);
+    return;
+  }
+  const int nv = len * vpr;  // only the valid rows are read
+  const i32x4* src = (is_v ? v_pad : k_pad) + (int64_t)b * max_kv * vpr;
+  i32x4* dst = (is_v ? v_pack : k_pack) + (int64_t)lo * vpr;
+  const int i0 = span * kCopySpan + threadIdx.x;
+  i32x4 r[kCopyPer];
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const int i = i0 + u * kCopyThreads;
+    if (i < nv) r[u] = __builtin_nontemporal_load(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyPer; ++u) {
+    const int i = i0 + u * kCopyThreads;
+    if (i < nv) dst[i] = r[u];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Host launchers (called by api.hip after argument validation)
 // ---------------------------------------------------------------------------------------
 static int copy_spans(int64_t vectors) { return (int)((vectors + kCopySpan - 1) / kCopySpan); }
@@ -208,6 +285,46 @@ hipError_t launch_ring_write(const void* k_src, const void* v_src, void* k_store
   hipLaunchKernelGGL(k_ring_write, grd, dim3(kCopyThreads), 0, s, (const i32x4*)k_src,
                      (const i32x4*)v_src, (i32x4*)k_store, (i32x4*)v_store, meta, B, mask, C,
                      n_slots, vpr, spans, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_roll_left(void* k_store, void* v_store, int B, int rows, int sink_rows,
+                            int shift_rows, int vpr, hipStream_t s) {
+  // Pieces of at most shift_rows rows, in increasing row order: piece p reads rows that no
+  // earlier piece writes and writes rows that earlier pieces have already read (stream order),
+  // so the overlapping move needs no staging copy.
+  const int64_t stride = (int64_t)rows * vpr;
+  for (int first = sink_rows + shift_rows; first < rows; first += shift_rows) {
+    const int n = rows - first < shift_rows ? rows - first : shift_rows;
+    const int nv = n * vpr;
+    const int spans = copy_spans(nv);
+    dim3 grd((unsigned)((int64_t)B * spans), v_store ? 2 : 1);
+    const i32x4* ks = (const i32x4*)k_store + (int64_t)first * vpr;
+    i32x4* kd = (i32x4*)k_store + (int64_t)(first - shift_rows) * vpr;
+    const i32x4* vs = v_store ? (const i32x4*)v_store + (int64_t)first * vpr : nullptr;
+    i32x4* vd = v_store ? (i32x4*)v_store + (int64_t)(first - shift_rows) * vpr : nullptr;
+    hipLaunchKernelGGL(k_move_block, grd, dim3(kCopyThreads), 0, s, ks, kd, vs, vd, stride, stride,
+                       nv, spans);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_ragged_metadata(const int32_t* lens, int B, int max_kv, int32_t* cu, int32_t* err,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(k_ragged_metadata, dim3(1), dim3(64), 0, s, lens, B, max_kv, cu, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_ragged(const void* k_pad, const void* v_pad, void* k_pack, void* v_pack,
+                              const int32_t* cu, int B, int max_kv, int packed_rows, int vpr,
+                              int32_t* err, hipStream_t s) {
+  const int spans = copy_spans((int64_t)max_kv * vpr);
+  dim3 grd((unsigned)((int64_t)B * spans), v_pack ? 2 : 1);
+  hipLaunchKernelGGL(k_pack_ragged, grd, dim3(kCopyThreads), 0, s, (const i32x4*)k_pad,
+                     (const i32x4*)v_pad, (i32x4*)k_pack, (i32x4*)v_pack, cu, max_kv, packed_rows,
+                     vpr, spans, err);
   return hipGetLastError();
 }
 

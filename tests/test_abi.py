@@ -149,3 +149,29 @@ def test_decode_step_host_errors():
     assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(p), None) == skv.SKV_ERR_UNSUPPORTED
     p = params(Tq=1)
     assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(p), None) == skv.SKV_ERR_NULL  # workspace
+
+
+def test_roll_and_pack_host_errors():
+    f = lib.kv_roll_left
+    # k_store, v_store, B, rows, sink_rows, shift_rows, Hkv, D, dtype, stream
+    assert f(None, None, 1, 8, 1, 2, 1, 64, skv.SKV_BF16, None) == skv.SKV_ERR_NULL
+    assert f(P, None, 1, 8, 1, 2, 1, 64, 9, None) == skv.SKV_ERR_DTYPE
+    assert f(P, None, 1, 8, 7, 2, 1, 64, skv.SKV_BF16, None) == skv.SKV_ERR_RANGE  # sink+shift > rows
+    assert f(P, None, 1, 8, -1, 2, 1, 64, skv.SKV_BF16, None) == skv.SKV_ERR_RANGE
+    assert f(P, None, 1, 8, 1, 0, 1, 64, skv.SKV_BF16, None) == skv.SKV_ERR_RANGE
+    assert f(BAD, None, 1, 8, 1, 2, 1, 64, skv.SKV_BF16, None) == skv.SKV_ERR_ALIGN
+    assert f(P, None, 1, 8, 1, 2, 1, 3, skv.SKV_BF16, None) == skv.SKV_ERR_ALIGN  # 6-byte rows
+    assert f(P, None, 1, 8, 6, 2, 1, 64, skv.SKV_BF16, None) == skv.SKV_OK      # nothing to move
+    assert f(P, None, 0, 8, 1, 2, 1, 64, skv.SKV_BF16, None) == skv.SKV_OK      # B = 0
+    g = lib.kv_ragged_metadata
+    assert g(None, 2, 8, P, None, None) == skv.SKV_ERR_NULL
+    assert g(P, 0, 8, P, None, None) == skv.SKV_ERR_SHAPE
+    assert g(P + 2, 2, 8, P, None, None) == skv.SKV_ERR_ALIGN
+    h = lib.kv_pack_ragged
+    # k_packed, v_packed, k_padded, v_padded, cu, B, max_kv, packed_rows, Hkv, D, dtype, err, stream
+    assert h(P, None, P, None, None, 2, 8, 16, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_NULL
+    assert h(P, P, P, None, P, 2, 8, 16, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_NULL
+    assert h(P, None, P, None, P, 2, 8, 16, 1, 64, 5, None, None) == skv.SKV_ERR_DTYPE
+    assert h(P, None, P, None, P, 0, 8, 16, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_SHAPE
+    assert h(BAD, None, P, None, P, 2, 8, 16, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_ALIGN
+    assert h(P, None, P, None, P, 2, 0, 16, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_OK  # nothing
