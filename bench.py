@@ -284,6 +284,22 @@ def bench_ring(torch, skv, SI, dev):
                 skv.attn_chunk_fwd(q, ks, vs, out, kv_len_dev=ring.kv_len, max_seqlen_kv=rows)
 
     seq_ms = time_gpu(torch, sequence, reps=3, warm=1)
+
+    def rolling_sequence():
+        # the comparison arm: the same chunk lifecycle on a chronological buffer that moves its
+        # retained non-sink rows left by one chunk whenever a new chunk does not fit
+        filled = 0
+        for c in range(W.n_chunks):
+            if filled + W.C > rows:
+                skv.kv_roll_left(ks, vs, W.sink * W.C, W.C)
+            else:
+                filled += W.C
+            for r in range(W.rewrites):
+                q, k, v = srcs[(c % 2) * 2 + (r % 2)]
+                skv.kv_write_indexed(ks, vs, k, v, start=filled - W.C)
+                skv.attn_chunk_fwd(q, ks, vs, out, kv_len=filled)
+
+    roll_seq_ms = time_gpu(torch, rolling_sequence, reps=3, warm=1)
     # saturated step: 7 valid slots
     ring.reset()
     for c in range(W.n_slots):
@@ -294,12 +310,16 @@ def bench_ring(torch, skv, SI, dev):
                                                          max_seqlen_kv=rows), reps=10)
     flush = make_flush(torch, dev)
     write_ms = time_gpu(torch, lambda: ring.write(srcs[0][1], srcs[0][2]), reps=10, flush=flush)
+    roll_ms = time_gpu(torch, lambda: skv.kv_roll_left(ks, vs, W.sink * W.C, W.C), reps=10, flush=flush)
     del flush
     reset_ms = time_gpu(torch, lambda: ring.reset(), reps=10)
     flop_sat = 4 * W.D * W.H * W.B * W.C * (W.n_slots * W.C)
     flop_seq = sum(4 * W.D * W.H * W.B * W.C * (min(c + 1, W.n_slots) * W.C) * W.rewrites
                    for c in range(W.n_chunks))
     wbytes = 2 * 2 * W.B * W.C * W.H * W.D * ELEM
+    moved = rows - W.sink * W.C - W.C  # retained non-sink rows moved per roll
+    rbytes = 2 * 2 * W.B * moved * W.H * W.D * ELEM
+    n_rolls = max(0, W.n_chunks - W.n_slots)
     return {
         "workload": "ring: B=2, 12 heads, D=128, bf16, chunks of 4680, 7 slots (1 sink), 12 chunks x 4 rewrites",
         "sequence_ms": seq_ms, "sequence_tflops": flop_seq / seq_ms * 1e-9,
@@ -309,6 +329,13 @@ def bench_ring(torch, skv, SI, dev):
         "ring_write_ms_cold": write_ms, "ring_write_gbs": wbytes / write_ms * 1e-6,
         "ring_write_frac_hbm": wbytes / write_ms * 1e-6 / HBM_PEAK_GBS,
         "reset_us": reset_ms * 1e3,
+        "rolling_arm": {
+            "what": "chronological buffer with roll-left past the sink (the path the ring replaces): "
+                    "same chunk lifecycle, host kv_len",
+            "sequence_ms": roll_seq_ms, "vs_ring_sequence": roll_seq_ms / seq_ms,
+            "roll_ms_cold": roll_ms, "roll_rows_moved": moved, "roll_bytes": rbytes,
+            "roll_gbs": rbytes / roll_ms * 1e-6, "rolls_per_sequence": n_rolls,
+            "ring_maintenance_bytes": 0},
     }
 
 
@@ -371,7 +398,16 @@ def bench_ragged(torch, skv, SI, dev):
         kpad[0, :lens[0]], kpad[1, :lens[1]] = kp[:lens[0]], kp[lens[0]:]
         vpad[0, :lens[0]], vpad[1, :lens[1]] = vp[:lens[0]], vp[lens[0]:]
         used = torch.tensor(list(lens), dtype=torch.int32, device=dev)
+        cu_buf = torch.empty(W.B + 1, dtype=torch.int32, device=dev)
+        kpk = torch.empty(total, W.H, W.D, dtype=torch.bfloat16, device=dev)
+        vpk = torch.empty_like(kpk)
+
+        def packed_total():  # metadata + gather + attention, what a caller pays per call
+            skv.kv_ragged_metadata(used, W.max_kv, cu_buf)
+            skv.kv_pack_ragged(kpad, vpad, cu_buf, kpk, vpk)
+            skv.attn_chunk_fwd(q, kpk, vpk, out, cu_seqlens_kv=cu_buf, max_seqlen_kv=W.max_kv)
         arms = {
+            "packed_total": packed_total,
             "packed": lambda: skv.attn_chunk_fwd(q, kp, vp, out, cu_seqlens_kv=cu, max_seqlen_kv=W.max_kv),
             "seqused": lambda: skv.attn_chunk_fwd(q, kpad, vpad, out, kv_len_dev=used, max_seqlen_kv=W.max_kv),
             "padded_masked": lambda: skv.attn_chunk_fwd(q, kpad, vpad, out, kv_len_dev=used, max_seqlen_kv=W.max_kv,
