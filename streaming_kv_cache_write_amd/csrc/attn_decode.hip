@@ -19,11 +19,13 @@
 //   * online softmax in fp32 with exp2 (scale folded), the row max over a tile by two
 //     cross-lane exchanges; the reference max moves only when a tile's max passes it by more
 //     than 2^8 in probability (the stale reference cancels in O / l);
-//   * the 4 wavefronts merge through LDS; with several splits each workgroup stores its
-//     unnormalised (m, l, o) to the caller's workspace with device-coherent (sc1) stores --
-//     the form agent-scope atomic stores take, visible to any XCD once complete -- and counts
-//     itself in; the last workgroup of (b, g) to arrive acquires (agent-scope fence) and merges
-//     the splits with weights exp(m_s - max m), then writes the output.
+//   * the 4 wavefronts merge through LDS, one thread per (row quad, column); with several
+//     splits each workgroup stores its unnormalised (m, l, o) to the caller's workspace with
+//     device-coherent (sc1) stores -- the form agent-scope atomic stores take, visible to any
+//     XCD once complete -- and counts itself in; the last workgroup of (b, g) to arrive reads
+//     them back with sc1 loads, first every split's weight exp(m_s - max m) / L (one
+//     half-wavefront per row, DPP reductions), then one weighted pass over the o partials,
+//     whose loads are already in flight, and writes the output.
 #include <type_traits>
 
 #include "common.h"
@@ -94,11 +96,6 @@ __host__ __device__ __forceinline__ size_t dec_o_floats(int B, int Hkv, int D, i
 __host__ __device__ __forceinline__ size_t dec_ml_floats(int B, int Hkv, int n_splits) {
   return ((size_t)B * Hkv * n_splits * kDecRows * 2 + 3) & ~(size_t)3;  // keep 16-byte alignment
 }
-// partial of query row r from split `split` of (b, g)
-__device__ __forceinline__ size_t dec_part_index(int b, int g, int split, int r, int Hkv,
-                                                 int n_splits) {
-  return (((size_t)b * Hkv + g) * n_splits + split) * kDecRows + r;
-}
 
 // Split partials cross XCDs, whose L2 caches are not coherent with each other. They are
 // stored and loaded with the sc1 cache policy -- device-coherent, as agent-scope atomic
@@ -106,7 +103,6 @@ __device__ __forceinline__ size_t dec_part_index(int b, int g, int split, int r,
 // sc1 load from any CU, with no cache write-back or invalidate.
 constexpr int kDeviceCoherent = 16;  // buffer-op cache policy bits: sc1
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0)
-typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* base, size_t floats) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(floats * sizeof(float)),
@@ -117,131 +113,161 @@ __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, size_t 
                    __float_as_uint(v.w)};
   __builtin_amdgcn_raw_buffer_store_b128(d, r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent);
 }
-__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, size_t fidx, float2 v) {
-  const u32x2 d = {__float_as_uint(v.x), __float_as_uint(v.y)};
-  __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent);
-}
 __device__ __forceinline__ float4 load_coherent4(__amdgpu_buffer_rsrc_t r, size_t fidx) {
   const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent);
   return make_float4(__uint_as_float(d[0]), __uint_as_float(d[1]), __uint_as_float(d[2]),
                      __uint_as_float(d[3]));
 }
-__device__ __forceinline__ float2 load_coherent2(__amdgpu_buffer_rsrc_t r, size_t fidx) {
-  const u32x2 d = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent);
-  return make_float2(__uint_as_float(d[0]), __uint_as_float(d[1]));
+
+// Partial layout: split `split` of (b, g) holds o as [4 row quads][D] float4 (rows 4q .. 4q+3
+// of one column in one float4), then (m, l) as 16 maxima followed by 16 sums.
+__device__ __forceinline__ size_t dec_o_quad(int b, int g, int split, int rq, int Hkv,
+                                             int n_splits, int D) {
+  return ((((size_t)b * Hkv + g) * n_splits + split) * 4 + rq) * D;  // in float4 units
+}
+__device__ __forceinline__ size_t dec_ml_base(int b, int g, int split, int Hkv, int n_splits) {
+  return (((size_t)b * Hkv + g) * n_splits + split) * (2 * kDecRows);
+}
+__device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t r, size_t fidx) {
+  return __uint_as_float(
+      __builtin_amdgcn_raw_buffer_load_b32(r, (int)(fidx * sizeof(float)), 0, kDeviceCoherent));
 }
 
-// Online-softmax state of one query row over 8 output columns.
-struct MergeState {
-  float M, L, o[8];
-};
-
-__device__ __forceinline__ void merge_init(MergeState& st) {
-  st.M = -INFINITY;
-  st.L = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) st.o[e] = 0.f;
+// Lane exchanges by DPP (every lane of the wavefront active): quad xor 1 and 2, and the two
+// mirrors, which with the quad steps reduce over each row of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+__device__ __forceinline__ float max32(float x) {  // over each 32-lane half of the wavefront
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppMirror>(x));
+  return fmaxf(x, __shfl_xor(x, 16, 64));
+}
+__device__ __forceinline__ float sum32(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  x += dpp_f<kDppMirror>(x);
+  return x + __shfl_xor(x, 16, 64);
 }
 
-// Output row r (= t * group + hh: query t, head g * group + hh), columns [8dc, 8dc + 8).
+__device__ __forceinline__ float f4_get(float4 v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Output rows 4rq .. 4rq+3 (those < R) at column col; row r = t * group + hh is query t of
+// head g * group + hh. v holds the normalised values.
 template <typename OutT>
-__device__ __forceinline__ void write_row(const AttnArgs& a, int D, int group, int b, int g, int r,
-                                          int dc, const MergeState& st) {
-  const int t = r / group, h = g * group + (r - t * group);
-  const float inv = st.L > 0.f ? 1.f / st.L : 0.f;  // L = 0: the batch element was rejected
-  OutT* out = (OutT*)a.out + (((int64_t)b * a.Tq + t) * a.Hq + h) * D + 8 * dc;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = from_f32<OutT>(st.o[e] * inv);
-  if (a.lse && dc == 0)
-    a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = st.L > 0.f ? st.M * a.scale + logf(st.L) : -INFINITY;
-}
-
-// Fold N partials (m, l, o) into st: the new max first, then independent weights and sums
-// (no chain of per-partial rescales).
-template <int N>
-__device__ __forceinline__ void fold_batch(MergeState& st, const float2* ml, const float4* oa,
-                                           const float4* ob, float c2) {
-  float mb = st.M;
-#pragma unroll
-  for (int u = 0; u < N; ++u) mb = fmaxf(mb, ml[u].x);
-  const float m_use = mb == -INFINITY ? 0.f : mb;
-  const float ws = __builtin_amdgcn_exp2f((st.M - m_use) * c2);
-  float L = st.L * ws, o[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = st.o[e] * ws;
-#pragma unroll
-  for (int u = 0; u < N; ++u) {
-    const float w = __builtin_amdgcn_exp2f((ml[u].x - m_use) * c2);
-    L = fmaf(w, ml[u].y, L);
-    o[0] = fmaf(w, oa[u].x, o[0]);
-    o[1] = fmaf(w, oa[u].y, o[1]);
-    o[2] = fmaf(w, oa[u].z, o[2]);
-    o[3] = fmaf(w, oa[u].w, o[3]);
-    o[4] = fmaf(w, ob[u].x, o[4]);
-    o[5] = fmaf(w, ob[u].y, o[5]);
-    o[6] = fmaf(w, ob[u].z, o[6]);
-    o[7] = fmaf(w, ob[u].w, o[7]);
-  }
-  st.M = mb;
-  st.L = L;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) st.o[e] = o[e];
-}
-
-// The last workgroup of (b, g), after its acquire: fold the n_splits partials of each used
-// row with ordinary (cached) loads. Thread t takes
-// (row, 8-column chunk) pair t / tpp and every tpp-th split from t % tpp; the tpp threads of a
-// pair (adjacent lanes of one wavefront) then combine by lane exchanges.
-template <int D, typename OutT>
-__device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, const float* ws_o,
-                                             const float* ws_ml, int b, int g, int n_splits) {
-  constexpr int CH = D / 8;  // 8-column chunks per row
+__device__ __forceinline__ void write_quad(const AttnArgs& a, int D, int group, int b, int g,
+                                           int rq, int col, float4 v) {
   const int R = a.Tq * group;
-  int rp = 1;
-  while (rp < R) rp <<= 1;   // rows padded to a power of two: pairs divide 256
-  const int tpp = 256 / (rp * CH) > 1 ? 256 / (rp * CH) : 1;
-  const int t = threadIdx.x;
-  const int pair = t / tpp, sub = t - pair * tpp;
-  const int r = pair / CH, dc = pair - r * CH;
-  const bool row_ok = r < R;
-  const float c2 = a.scale_log2;
-  MergeState st;
-  merge_init(st);
-  constexpr int kBatch = 8;
-  for (int s0 = sub; s0 < n_splits; s0 += kBatch * tpp) {
-    float2 ml[kBatch];
-    float4 oa[kBatch], ob[kBatch];
+  int t = (4 * rq) / group, hh = 4 * rq - t * group;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {  // every load of the batch issued before any use
-      const int sp = s0 + u * tpp;
-      const bool ok = row_ok && sp < n_splits;
-      const size_t pi = dec_part_index(b, g, ok ? sp : 0, ok ? r : 0, a.Hkv, n_splits);
-      ml[u] = *(const float2*)(ws_ml + 2 * pi);
-      oa[u] = *(const float4*)(ws_o + pi * D + 8 * dc);
-      ob[u] = *(const float4*)(ws_o + pi * D + 8 * dc + 4);
-      if (!ok) {  // contributes weight 0 and finite values only
-        ml[u] = make_float2(-INFINITY, 0.f);
-        oa[u] = ob[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < 4; ++j) {
+    if (4 * rq + j < R)
+      ((OutT*)a.out)[(((int64_t)b * a.Tq + t) * a.Hq + g * group + hh) * D + col] =
+          from_f32<OutT>(f4_get(v, j));
+    if (++hh == group) {
+      hh = 0;
+      ++t;
+    }
+  }
+}
+__device__ __forceinline__ void write_lse(const AttnArgs& a, int group, int b, int g, int r,
+                                          float M, float L) {
+  const int t = r / group, h = g * group + (r - t * group);
+  a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = L > 0.f ? M * a.scale + logf(L) : -INFINITY;
+}
+
+// The last workgroup of (b, g): merge the n_splits partials. Every load is unconditional
+// (indices clamped, invalid entries neutralised afterwards), so no load waits on a branch. The
+// (m, l) loads go first, then the first batch of o loads; step 1 -- thread (row r, split s),
+// 32 splits per half-wavefront -- reduces over the splits to the weight exp2((m_s - M) c2) / L
+// of each partial (L = the weighted sum of the l_s), kept in LDS, while the o loads are in
+// flight. Step 2: thread (row quad, column, split residue mod tpp) sums its splits' weighted
+// o; the tpp threads of a pair are adjacent lanes and add by DPP.
+template <int D, typename OutT>
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, int RQ,
+                                             __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml,
+                                             float (*wt)[kDecRows], int b, int g, int n_splits) {
+  constexpr int kMB = 16;  // o loads in flight per thread
+  const int R = a.Tq * group, rows = 4 * RQ;
+  const float c2 = a.scale_log2;
+  const int pairs = RQ * D;  // (row quad, column)
+  const int tpp = pairs <= 64 ? 4 : pairs <= 128 ? 2 : 1;
+  const int t = threadIdx.x, sub = t & (tpp - 1), p0 = t / tpp;
+  const int p_step = 256 / tpp;
+  const int last_split = n_splits - 1;
+
+  float mm[2], ll[2];  // (m, l) of (row q / 32, split q % 32) for q = t, t + 256
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = t + 256 * k;
+    const size_t base = dec_ml_base(b, g, min(q & 31, last_split), a.Hkv, n_splits);
+    const int r = min(q >> 5, rows - 1);
+    mm[k] = load_coherent1(rml, base + r);
+    ll[k] = load_coherent1(rml, base + kDecRows + r);
+  }
+  float4 ob[kMB];
+  auto load_batch = [&](int p, int s0) {
+    const int pc = min(p, pairs - 1);
+    const int rq = pc / D, col = pc - rq * D;
+#pragma unroll
+    for (int i = 0; i < kMB; ++i)
+      ob[i] = load_coherent4(
+          ro, (dec_o_quad(b, g, min(s0 + i * tpp, last_split), rq, a.Hkv, n_splits, D) + col) * 4);
+  };
+  load_batch(p0, sub);
+
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = t + 256 * k, r = q >> 5, sp = q & 31;
+    const bool ok = r < rows && sp < n_splits;
+    // a clamped split index repeats the row's last split, which leaves the max unchanged;
+    // it gets weight 0 (its l, a finite partial of this launch, then adds nothing)
+    const float M = max32(mm[k]);
+    const float e = __builtin_amdgcn_exp2f((mm[k] - (M == -INFINITY ? 0.f : M)) * c2);
+    const float w = ok ? e : 0.f;
+    const float L = sum32(w * ll[k]);
+    if (ok) wt[sp][r] = L > 0.f ? w / L : 0.f;
+    if (ok && sp == 0 && r < R && a.lse) write_lse(a, group, b, g, r, M, L);
+  }
+  __syncthreads();
+
+  for (int p = p0; p - p0 < pairs; p += p_step) {  // the same trip count in every thread
+    const int pc = min(p, pairs - 1);
+    const int rq = pc / D, col = pc - rq * D;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = sub; s0 < n_splits; s0 += kMB * tpp) {
+      if (p != p0 || s0 != sub) load_batch(p, s0);
+      float4 w4[kMB];
+#pragma unroll
+      for (int i = 0; i < kMB; ++i) w4[i] = *(const float4*)&wt[min(s0 + i * tpp, last_split)][4 * rq];
+#pragma unroll
+      for (int i = 0; i < kMB; ++i) {
+        const bool ok = s0 + i * tpp < n_splits;
+        acc = make_float4(fmaf(ok ? w4[i].x : 0.f, ob[i].x, acc.x), fmaf(ok ? w4[i].y : 0.f, ob[i].y, acc.y),
+                          fmaf(ok ? w4[i].z : 0.f, ob[i].z, acc.z), fmaf(ok ? w4[i].w : 0.f, ob[i].w, acc.w));
       }
     }
-    fold_batch<kBatch>(st, ml, oa, ob, c2);
+    if (tpp > 1) {
+      acc.x += dpp_f<kDppXor1>(acc.x);
+      acc.y += dpp_f<kDppXor1>(acc.y);
+      acc.z += dpp_f<kDppXor1>(acc.z);
+      acc.w += dpp_f<kDppXor1>(acc.w);
+    }
+    if (tpp > 2) {
+      acc.x += dpp_f<kDppXor2>(acc.x);
+      acc.y += dpp_f<kDppXor2>(acc.y);
+      acc.z += dpp_f<kDppXor2>(acc.z);
+      acc.w += dpp_f<kDppXor2>(acc.w);
+    }
+    if (sub == 0 && p < pairs) write_quad<OutT>(a, D, group, b, g, rq, col, acc);
   }
-  // the tpp threads of a pair: common max first, then plain sums of the rescaled states
-  float M = st.M;
-  for (int off = tpp >> 1; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  {
-    const float w = __builtin_amdgcn_exp2f((st.M - (M == -INFINITY ? 0.f : M)) * c2);
-    st.L *= w;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.o[e] *= w;
-    st.M = M;
-  }
-  for (int off = tpp >> 1; off > 0; off >>= 1) {
-    st.L += __shfl_xor(st.L, off, 64);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.o[e] += __shfl_xor(st.o[e], off, 64);
-  }
-  if (row_ok && sub == 0) write_row<OutT>(a, D, group, b, g, r, dc, st);
 }
 
 // Workgroup = kDecWaves wavefronts per (split, KV head g, batch element b). The split covers
@@ -266,15 +292,16 @@ __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int 
   constexpr int DQ = D / 32;   // 32-wide d steps of S^T
   constexpr int CB = D / 16;   // 16-column output blocks
   constexpr int VU = D / 32;   // 16-byte V pieces per lane per tile
-  constexpr int CH = D / 8;    // 8-column chunks per row
   // V tile row pitch: 32 bytes past a multiple of 256, so the 8 key rows one half-wavefront
   // reads in a transposed read fall on distinct banks
   constexpr int LDV = D == 128 ? D + 16 : D + 80;
   __shared__ __attribute__((aligned(16))) union {
     TP v[kDecWaves][kDecTile * LDV];     // per-wavefront V tile
-    float o[kDecWaves][kDecRows][D];     // after the tile loop: per-wavefront outputs
+    float4 o[kDecWaves][4][D];           // after the tile loop: per-wavefront o, by row quad
+    float wt[kDecMaxSplits][kDecRows];   // cross-split merge: weight of each partial
   } sm;
-  __shared__ float st_m[kDecWaves][kDecRows], st_l[kDecWaves][kDecRows];
+  __shared__ __attribute__((aligned(16))) float st_m[kDecWaves][kDecRows];
+  __shared__ __attribute__((aligned(16))) float st_l[kDecWaves][kDecRows];
   __shared__ int last_s;
 
   // Workgroup -> (split, b, g). Dispatch deals consecutive workgroup ids to the 8 XCDs in turn;
@@ -468,45 +495,71 @@ __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int 
   // row n16's sum: the four lane groups hold different keys of it
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
+  const int RQ = (R + 3) >> 2;  // row quads in use
   __syncthreads();  // every wavefront is done with its V tile: the union becomes the output stage
   if (G == 0) {
     st_m[wave][n16] = m;
     st_l[wave][n16] = lsum;
   }
+  if (G < RQ) {  // lane (G, n16) holds rows 4G .. 4G+3 of columns 16cb + n16
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sm.o[wave][4 * G + j][16 * cb + n16] = o[cb][j];
+    for (int cb = 0; cb < CB; ++cb) sm.o[wave][G][16 * cb + n16] = make_float4(o[cb][0], o[cb][1], o[cb][2], o[cb][3]);
+  }
   __syncthreads();
 
-  // merge the wavefronts: thread -> (row, 8-column chunk); 256 threads cover 16 rows x D/8
-  const int r = threadIdx.x / CH, dc = threadIdx.x - r * CH;
-  const bool mine = r < R;
-  MergeState st;
-  merge_init(st);
-  if (mine) {
-    float2 ml[kDecWaves];
-    float4 oa[kDecWaves], ob[kDecWaves];
+  // merge the wavefronts: thread -> (row quad, column)
+  const __amdgpu_buffer_rsrc_t ro = ws_rsrc(ws_o, dec_o_floats(a.B, a.Hkv, D, n_splits));
+  const __amdgpu_buffer_rsrc_t rml = ws_rsrc(ws_ml, dec_ml_floats(a.B, a.Hkv, n_splits));
+  for (int p = threadIdx.x; p < RQ * D; p += 64 * kDecWaves) {
+    const int rq = p / D, col = p - rq * D;
+    float4 mw[kDecWaves], lw[kDecWaves], ow[kDecWaves];
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      ml[w] = make_float2(st_m[w][r], st_l[w][r]);
-      oa[w] = *(const float4*)&sm.o[w][r][8 * dc];
-      ob[w] = *(const float4*)&sm.o[w][r][8 * dc + 4];
+      mw[w] = *(const float4*)&st_m[w][4 * rq];
+      lw[w] = *(const float4*)&st_l[w][4 * rq];
+      ow[w] = sm.o[w][rq][col];
     }
-    fold_batch<kDecWaves>(st, ml, oa, ob, c2);
+    float Mj[4], Lj[4], Oj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, f4_get(mw[w], j));
+      const float mu = M == -INFINITY ? 0.f : M;
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        const float e = __builtin_amdgcn_exp2f((f4_get(mw[w], j) - mu) * c2);
+        L = fmaf(e, f4_get(lw[w], j), L);
+        O = fmaf(e, f4_get(ow[w], j), O);
+      }
+      Mj[j] = M;
+      Lj[j] = L;
+      Oj[j] = O;
+    }
+    if (n_splits == 1) {  // the workgroup saw every key: its merge is the output
+      float4 v;
+      v.x = Lj[0] > 0.f ? Oj[0] / Lj[0] : 0.f;  // L = 0: the batch element was rejected
+      v.y = Lj[1] > 0.f ? Oj[1] / Lj[1] : 0.f;
+      v.z = Lj[2] > 0.f ? Oj[2] / Lj[2] : 0.f;
+      v.w = Lj[3] > 0.f ? Oj[3] / Lj[3] : 0.f;
+      write_quad<OutT>(a, D, group, b, g, rq, col, v);
+      if (a.lse && col == 0)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (4 * rq + j < R) write_lse(a, group, b, g, 4 * rq + j, Mj[j], Lj[j]);
+    } else {
+      store_coherent(ro, (dec_o_quad(b, g, split, rq, a.Hkv, n_splits, D) + col) * 4,
+                     make_float4(Oj[0], Oj[1], Oj[2], Oj[3]));
+      if (col == 0) {
+        const size_t base = dec_ml_base(b, g, split, a.Hkv, n_splits);
+        store_coherent(rml, base + 4 * rq, make_float4(Mj[0], Mj[1], Mj[2], Mj[3]));
+        store_coherent(rml, base + kDecRows + 4 * rq, make_float4(Lj[0], Lj[1], Lj[2], Lj[3]));
+      }
+    }
   }
 
-  if (n_splits == 1) {  // the workgroup saw every key: its merge is the output
-    if (mine) write_row<OutT>(a, D, group, b, g, r, dc, st);
-  } else {
-    const __amdgpu_buffer_rsrc_t ro = ws_rsrc(ws_o, dec_o_floats(a.B, a.Hkv, D, n_splits));
-    const __amdgpu_buffer_rsrc_t rml = ws_rsrc(ws_ml, dec_ml_floats(a.B, a.Hkv, n_splits));
-    if (mine) {
-      const size_t pi = dec_part_index(b, g, split, r, a.Hkv, n_splits);
-      store_coherent(ro, pi * D + 8 * dc, make_float4(st.o[0], st.o[1], st.o[2], st.o[3]));
-      store_coherent(ro, pi * D + 8 * dc + 4, make_float4(st.o[4], st.o[5], st.o[6], st.o[7]));
-      if (dc == 0) store_coherent(rml, 2 * pi, make_float2(st.M, st.L));
-    }
+  if (n_splits > 1) {
     // every store of the workgroup has completed before its arrival is counted
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
@@ -519,10 +572,11 @@ __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int 
     }
     __syncthreads();
     if (!last_s) return;
-    // acquire at agent scope: drop cached copies (L1, and L2 lines another XCD may have
-    // rewritten) so the loads below see every split's completed stores
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    merge_splits<D, OutT>(a, group, ws_o, ws_ml, b, g, n_splits);
+    // The partials are read with sc1 loads, the form agent-scope atomic loads take: they see
+    // every store that completed before its workgroup was counted, with no cache invalidate.
+    // The fence keeps the compiler from moving them above the arrival count.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    merge_splits<D, OutT>(a, group, RQ, ro, rml, sm.wt, b, g, n_splits);
   }
   if constexpr (FUSED) {
     // this workgroup wrote (b, g)'s output; every workgroup of the launch read the cursor
