@@ -29,6 +29,9 @@ Modules:
   roll-left copy that the ring replaces (the comparison arm).
 * ``oracle.ragged`` -- packing of ragged K/V (each branch's valid rows
   concatenated) and its prefix-sum metadata.
+* ``oracle.rope`` -- keys rotated at their absolute positions before the cache
+  write (fp64 rotation, then the cache dtype's rounding), and the positions of
+  ring chunks.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, brute force, library routines (torch CPU fp64 SDPA) and the values the
