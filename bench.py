@@ -311,6 +311,23 @@ def bench_ring(torch, skv, SI, dev):
     flush = make_flush(torch, dev)
     write_ms = time_gpu(torch, lambda: ring.write(srcs[0][1], srcs[0][2]), reps=10, flush=flush)
     roll_ms = time_gpu(torch, lambda: skv.kv_roll_left(ks, vs, W.sink * W.C, W.C), reps=10, flush=flush)
+    # keys rotated at their absolute positions before storage: fused into the ring write, and
+    # the unfused path (a separate rotation by torch in fp32, then the plain write) beside it
+    half = W.D // 2
+    inv = torch.pow(torch.tensor(10000.0, dtype=torch.float64, device=dev),
+                    -torch.arange(half, dtype=torch.float64, device=dev) * 2.0 / W.D)
+    rope_ms = time_gpu(torch, lambda: ring.write_rope(srcs[0][1], srcs[0][2], inv), reps=10, flush=flush)
+    ang = ((int(ring.counter[0].item()) - 1) * W.C
+           + torch.arange(W.C, dtype=torch.float64, device=dev))[:, None] * inv[None, :]
+    cos, sin = ang.cos().float()[None, :, None, :], ang.sin().float()[None, :, None, :]
+
+    def unfused_rope_write():
+        x = srcs[0][1].float()
+        a, b = x[..., :half], x[..., half:]
+        ring.write(torch.cat([a * cos - b * sin, a * sin + b * cos], dim=-1).to(torch.bfloat16),
+                   srcs[0][2])
+
+    unfused_ms = time_gpu(torch, unfused_rope_write, reps=10, flush=flush)
     del flush
     reset_ms = time_gpu(torch, lambda: ring.reset(), reps=10)
     flop_sat = 4 * W.D * W.H * W.B * W.C * (W.n_slots * W.C)
@@ -329,6 +346,13 @@ def bench_ring(torch, skv, SI, dev):
         "ring_write_ms_cold": write_ms, "ring_write_gbs": wbytes / write_ms * 1e-6,
         "ring_write_frac_hbm": wbytes / write_ms * 1e-6 / HBM_PEAK_GBS,
         "reset_us": reset_ms * 1e3,
+        "rope_write": {
+            "what": "kv_ring_write_rope: K rotated at chunk_id*C+t (fp64) as it is written, V copied; "
+                    "unfused arm: torch fp32 rotation of K, then kv_ring_write",
+            "fused_ms_cold": rope_ms, "fused_gbs": wbytes / rope_ms * 1e-6,
+            "fused_frac_hbm": wbytes / rope_ms * 1e-6 / HBM_PEAK_GBS,
+            "unfused_ms_cold": unfused_ms, "unfused_vs_fused": unfused_ms / rope_ms,
+            "vs_plain_write": rope_ms / write_ms},
         "rolling_arm": {
             "what": "chronological buffer with roll-left past the sink (the path the ring replaces): "
                     "same chunk lifecycle, host kv_len",

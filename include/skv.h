@@ -86,6 +86,34 @@ skv_status kv_write_indexed(void* k_cache, void* v_cache, const void* k_src, con
                             int Hkv, int D, int dtype, int32_t* err_dev, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Writes with keys rotated at their absolute positions [FD, proposed boundary: keys whose
+ * rotary embedding is applied before the cache write, at absolute positions]
+ *
+ * The page gives no formula; these entry points implement 1-D rotary embedding. For each key
+ * row (every head) and pair index i < D/2, the coordinates (a, b) of pair i -- (i, i + D/2)
+ * for SKV_ROPE_HALF, (2i, 2i + 1) for SKV_ROPE_INTERLEAVED -- become
+ *     (a cos(theta) - b sin(theta), a sin(theta) + b cos(theta)),  theta = pos * inv_freq[i],
+ * computed in fp64 (no fused multiply-add), rounded to fp32 and then to the cache dtype
+ * (round to nearest even). inv_freq_dev: double [D/2] on the device, 8-byte aligned, the
+ * caller's frequencies (e.g. base^(-2i/D)). V rows are stored unchanged. D must be a power of
+ * two in [16, 4096] (else SKV_ERR_SHAPE); other errors as for the plain writes.
+ *
+ * kv_write_indexed_rope: kv_write_indexed with K rotated at pos = its destination row
+ *     (index_dev[t], or start + t when index_dev is NULL).
+ * kv_ring_write_rope: kv_ring_write with K rotated at pos = chunk_id * chunk + t, where
+ *     chunk_id counts the chunks reserved before the current one since the last reset (the
+ *     sink chunk is 0), read from the ring's device metadata -- so the repeated denoising
+ *     writes of one chunk rotate identically, and the positions follow time, not slots.
+ * ------------------------------------------------------------------------------------ */
+typedef enum { SKV_ROPE_HALF = 0, SKV_ROPE_INTERLEAVED = 1 } skv_rope_layout;
+
+skv_status kv_write_indexed_rope(void* k_cache, void* v_cache, const void* k_src,
+                                 const void* v_src, const int64_t* index_dev, int64_t start, int B,
+                                 int cap, int n, int Hkv, int D, int dtype,
+                                 const double* inv_freq_dev, int rope_layout, int32_t* err_dev,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Device write cursor [LB, What this is and isn't: the write offset and the read slice must
  * stop being host integers for graph capture; FD, proposed boundary]
  *
@@ -135,6 +163,11 @@ skv_status kv_ring_reserve(skv_ring* ring, const uint8_t* batch_mask_dev, void* 
 /* k_src/v_src: [B, chunk, Hkv, D]; v_src NULL iff the ring has no V storage. */
 skv_status kv_ring_write(skv_ring* ring, const void* k_src, const void* v_src,
                          const uint8_t* batch_mask_dev, int32_t* err_dev, void* stream);
+/* kv_ring_write with keys rotated at their chronological positions (see the section on
+   rotary writes above). */
+skv_status kv_ring_write_rope(skv_ring* ring, const void* k_src, const void* v_src,
+                              const double* inv_freq_dev, int rope_layout,
+                              const uint8_t* batch_mask_dev, int32_t* err_dev, void* stream);
 skv_status kv_ring_reset(skv_ring* ring, const uint8_t* batch_mask_dev, void* stream);
 const int32_t* kv_ring_kv_len_dev(const skv_ring* ring); /* valid[B], device */
 const int32_t* kv_ring_slot_dev(const skv_ring* ring);   /* slot[B], device */

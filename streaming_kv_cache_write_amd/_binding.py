@@ -26,6 +26,7 @@ STATUS_NAMES = ["SKV_OK", "SKV_ERR_NULL", "SKV_ERR_SHAPE", "SKV_ERR_RANGE", "SKV
                 "SKV_ERR_ALIGN", "SKV_ERR_UNSUPPORTED", "SKV_ERR_HIP"]
 SKV_F32, SKV_F16, SKV_BF16 = 0, 1, 2
 MASK_NONE, MASK_CAUSAL, MASK_BLOCK_CAUSAL = 0, 1, 2
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1  # pair (i, i + D/2) or (2i, 2i + 1)
 FULL_CAPACITY_MASKED = 1
 DEV_INDEX_RANGE, DEV_KV_LEN, DEV_CU_SEQLENS, DEV_RING_UNRESERVED, DEV_CURSOR_FULL = 1, 2, 4, 8, 16
 
@@ -60,11 +61,14 @@ _SIGS = {
     "skv_last_error": (ctypes.c_char_p, []),
     "skv_version": (ctypes.c_char_p, []),
     "kv_write_indexed": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "kv_write_indexed_rope": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i, _i, _i, _i, _i, _i, _vp, _i,
+                                   _vp, _vp]),
     "kv_cursor_advance": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "kv_ring_meta_bytes": (_sz, [_i]),
     "kv_ring_create": (_i, [ctypes.POINTER(_vp), _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "kv_ring_reserve": (_i, [_vp, _vp, _vp]),
     "kv_ring_write": (_i, [_vp, _vp, _vp, _vp, _vp, _vp]),
+    "kv_ring_write_rope": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "kv_ring_reset": (_i, [_vp, _vp, _vp]),
     "kv_ring_kv_len_dev": (_vp, [_vp]),
     "kv_ring_slot_dev": (_vp, [_vp]),
@@ -132,6 +136,35 @@ def kv_write_indexed(k_cache, v_cache, k_src, v_src, index=None, start: int = 0,
     _check(lib.kv_write_indexed(_ptr(k_cache), _ptr(v_cache), _ptr(k_src), _ptr(v_src), _ptr(index),
                                 int(start), B, cap, n, Hkv, D, dtype_code(k_cache.dtype), _ptr(err),
                                 _stream(k_cache.device)))
+
+
+def _inv_freq(inv_freq, D: int):
+    _dev_tensor(inv_freq, "inv_freq", torch.float64)
+    if inv_freq.numel() != D // 2:
+        raise ValueError(f"inv_freq must hold D/2 = {D // 2} frequencies (got {inv_freq.numel()})")
+    return inv_freq
+
+
+def kv_write_indexed_rope(k_cache, v_cache, k_src, v_src, inv_freq, rope_layout: int = ROPE_HALF,
+                          index=None, start: int = 0, err=None):
+    """kv_write_indexed with K rotated at its destination row: inv_freq float64 [D/2] on the
+    device, rope_layout ROPE_HALF or ROPE_INTERLEAVED."""
+    _dev_tensor(k_cache, "k_cache")
+    B, cap, Hkv, D = k_cache.shape
+    _dev_tensor(k_src, "k_src", k_cache.dtype)
+    if v_cache is not None:
+        _dev_tensor(v_cache, "v_cache", k_cache.dtype)
+        _dev_tensor(v_src, "v_src", k_cache.dtype)
+    if index is not None:
+        _dev_tensor(index, "index", torch.int64)
+    if err is not None:
+        _dev_tensor(err, "err", torch.int32)
+    _inv_freq(inv_freq, D)
+    n = k_src.shape[1]
+    _check(lib.kv_write_indexed_rope(_ptr(k_cache), _ptr(v_cache), _ptr(k_src), _ptr(v_src),
+                                     _ptr(index), int(start), B, cap, n, Hkv, D,
+                                     dtype_code(k_cache.dtype), _ptr(inv_freq), int(rope_layout),
+                                     _ptr(err), _stream(k_cache.device)))
 
 
 def kv_cursor_advance(cursor, n: int, cap: int, index_out, kv_len_out=None, err=None):
@@ -236,6 +269,23 @@ class Ring:
             raise ValueError(f"source must be [B={self.B}, chunk={self.chunk}, Hkv, D]")
         _check(lib.kv_ring_write(self._h, _ptr(k_src), _ptr(v_src), _ptr(batch_mask), _ptr(err),
                                  _stream(self.k_store.device)))
+
+    def write_rope(self, k_src, v_src, inv_freq, rope_layout: int = ROPE_HALF, batch_mask=None,
+                   err=None):
+        """write() with K rotated at chunk_id * chunk + t (chunk_id since the last reset)."""
+        _dev_tensor(k_src, "k_src", self.k_store.dtype)
+        if v_src is not None:
+            _dev_tensor(v_src, "v_src", self.k_store.dtype)
+        if batch_mask is not None:
+            _dev_tensor(batch_mask, "batch_mask", torch.uint8)
+        if err is not None:
+            _dev_tensor(err, "err", torch.int32)
+        if k_src.shape[0] != self.B or k_src.shape[1] != self.chunk:
+            raise ValueError(f"source must be [B={self.B}, chunk={self.chunk}, Hkv, D]")
+        _inv_freq(inv_freq, self.k_store.shape[3])
+        _check(lib.kv_ring_write_rope(self._h, _ptr(k_src), _ptr(v_src), _ptr(inv_freq),
+                                      int(rope_layout), _ptr(batch_mask), _ptr(err),
+                                      _stream(self.k_store.device)))
 
     def reset(self, batch_mask=None):
         if batch_mask is not None:

@@ -21,6 +21,12 @@ hipError_t launch_roll_left(void*, void*, int, int, int, int, int, hipStream_t);
 hipError_t launch_ragged_metadata(const int32_t*, int, int, int32_t*, int32_t*, hipStream_t);
 hipError_t launch_pack_ragged(const void*, const void*, void*, void*, const int32_t*, int, int, int,
                               int, int32_t*, hipStream_t);
+hipError_t launch_write_indexed_rope(const void*, const void*, void*, void*, const int64_t*, int64_t,
+                                     int, int, int, int, int, int, const double*, int, int32_t*,
+                                     hipStream_t);
+hipError_t launch_ring_write_rope(const void*, const void*, void*, void*, int32_t*, int,
+                                  const uint8_t*, int, int, int, int, int, const double*, int,
+                                  int32_t*, hipStream_t);
 hipError_t launch_attn_f32(const AttnArgs&, int, hipStream_t);
 hipError_t launch_attn_flash(const AttnArgs&, int, int, int, hipStream_t);
 hipError_t launch_attn_decode(const AttnArgs&, int, int, int, void*, int, hipStream_t);
@@ -122,6 +128,18 @@ skv_status validate_attn(const void* q, const void* k, const void* v, const void
   return SKV_OK;
 }
 
+// rotary-write arguments: frequency table, pair layout, a head size the kernels tile by
+// (8 coordinate pairs per thread, 256 threads per workgroup)
+skv_status check_rope(const double* inv_freq_dev, int rope_layout, int D) {
+  if (!inv_freq_dev) return fail(SKV_ERR_NULL, "inv_freq_dev is NULL");
+  if ((uintptr_t)inv_freq_dev & 7) return fail(SKV_ERR_ALIGN, "inv_freq_dev must be 8-byte aligned");
+  if (rope_layout != SKV_ROPE_HALF && rope_layout != SKV_ROPE_INTERLEAVED)
+    return fail(SKV_ERR_RANGE, "unknown rope_layout %d", rope_layout);
+  if (D < 16 || D > 4096 || (D & (D - 1)))
+    return fail(SKV_ERR_SHAPE, "rotary writes need D a power of two in [16, 4096] (got %d)", D);
+  return SKV_OK;
+}
+
 }  // namespace
 
 struct skv_ring {
@@ -159,6 +177,32 @@ skv_status kv_write_indexed(void* k_cache, void* v_cache, const void* k_src, con
   return hip_status(launch_write_indexed(k_src, v_src, k_cache, v_cache, index_dev, start, B, n,
                                          cap, (int)(row_bytes / 16), err_dev, (hipStream_t)stream),
                     "kv_write_indexed launch");
+}
+
+skv_status kv_write_indexed_rope(void* k_cache, void* v_cache, const void* k_src,
+                                 const void* v_src, const int64_t* index_dev, int64_t start, int B,
+                                 int cap, int n, int Hkv, int D, int dtype,
+                                 const double* inv_freq_dev, int rope_layout, int32_t* err_dev,
+                                 void* stream) {
+  if (!k_cache || !k_src) return fail(SKV_ERR_NULL, "k_cache and k_src must be non-NULL");
+  if ((v_cache == nullptr) != (v_src == nullptr))
+    return fail(SKV_ERR_NULL, "v_cache and v_src must both be given or both be NULL");
+  if (!elem_bytes(dtype)) return fail(SKV_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (B < 0 || n < 0 || cap < 1 || Hkv < 1 || D < 1)
+    return fail(SKV_ERR_SHAPE, "bad sizes B=%d cap=%d n=%d Hkv=%d D=%d", B, cap, n, Hkv, D);
+  const skv_status rs = check_rope(inv_freq_dev, rope_layout, D);
+  if (rs != SKV_OK) return rs;
+  if (!aligned16(k_cache) || !aligned16(k_src) || !aligned16(v_cache) || !aligned16(v_src))
+    return fail(SKV_ERR_ALIGN, "cache and source pointers must be 16-byte aligned");
+  if (!index_dev && (start < 0 || start + n > cap))
+    return fail(SKV_ERR_RANGE, "rows [%lld, %lld) outside the cache of %d rows", (long long)start,
+                (long long)(start + n), cap);
+  if ((int64_t)B * n > 0x7fffffff) return fail(SKV_ERR_SHAPE, "B*n too large");
+  if (B == 0 || n == 0) return ok();
+  return hip_status(launch_write_indexed_rope(k_src, v_src, k_cache, v_cache, index_dev, start, B,
+                                              n, cap, Hkv, D, dtype, inv_freq_dev, rope_layout,
+                                              err_dev, (hipStream_t)stream),
+                    "kv_write_indexed_rope launch");
 }
 
 skv_status kv_cursor_advance(int32_t* cursor_dev, int n, int cap, int B, int64_t* index_out_dev,
@@ -221,6 +265,23 @@ skv_status kv_ring_write(skv_ring* r, const void* k_src, const void* v_src,
                                       batch_mask_dev, r->chunk, r->n_slots, r->vpr, err_dev,
                                       (hipStream_t)stream),
                     "kv_ring_write launch");
+}
+
+skv_status kv_ring_write_rope(skv_ring* r, const void* k_src, const void* v_src,
+                              const double* inv_freq_dev, int rope_layout,
+                              const uint8_t* batch_mask_dev, int32_t* err_dev, void* stream) {
+  if (!r) return fail(SKV_ERR_NULL, "ring is NULL");
+  if (!k_src) return fail(SKV_ERR_NULL, "k_src is NULL");
+  if ((r->v_store == nullptr) != (v_src == nullptr))
+    return fail(SKV_ERR_NULL, "v_src must be given iff the ring has V storage");
+  const skv_status rs = check_rope(inv_freq_dev, rope_layout, r->D);
+  if (rs != SKV_OK) return rs;
+  if (!aligned16(k_src) || !aligned16(v_src)) return fail(SKV_ERR_ALIGN, "sources must be 16-byte aligned");
+  return hip_status(launch_ring_write_rope(k_src, v_src, r->k_store, r->v_store, r->meta, r->B,
+                                           batch_mask_dev, r->chunk, r->n_slots, r->Hkv, r->D,
+                                           r->dtype, inv_freq_dev, rope_layout, err_dev,
+                                           (hipStream_t)stream),
+                    "kv_ring_write_rope launch");
 }
 
 skv_status kv_ring_reset(skv_ring* r, const uint8_t* batch_mask_dev, void* stream) {

@@ -16,6 +16,7 @@
 // so that write is a plain span copy with the slot read once per workgroup. The kernels are
 // HBM-bound: each byte is read once and written once.
 #include "common.h"
+#include "ring_meta.h"
 
 namespace skv {
 
@@ -76,23 +77,8 @@ k_cursor_advance(int32_t* cursor, int n, int cap, int B, int64_t* index_out, int
 }
 
 // ---------------------------------------------------------------------------------------
-// Ring metadata: int32 [4][B] = counter, slot, pending, valid (structure of arrays, so
-// valid[] is directly the [B] kv_len vector attention reads).
+// Ring (metadata layout and helpers in ring_meta.h)
 // ---------------------------------------------------------------------------------------
-struct RingMeta {
-  int32_t* counter;
-  int32_t* slot;
-  int32_t* pending;
-  int32_t* valid;
-};
-
-__device__ __forceinline__ RingMeta ring_meta(int32_t* meta, int B) {
-  return RingMeta{meta, meta + B, meta + 2 * B, meta + 3 * B};
-}
-
-__device__ __forceinline__ bool selected(const uint8_t* mask, int b) {
-  return mask == nullptr || mask[b] != 0;
-}
 
 // Reset (also the initialisation): forget every chunk, keep the storage untouched.
 __global__ void k_ring_reset(int32_t* meta, int B, const uint8_t* mask) {
@@ -129,20 +115,7 @@ k_ring_write(const i32x4* __restrict__ k_src, const i32x4* __restrict__ v_src,
              i32x4* __restrict__ k_store, i32x4* __restrict__ v_store, int32_t* meta, int B,
              const uint8_t* mask, int C, int n_slots, int vpr, int spans, int32_t* err) {
   RingMeta m = ring_meta(meta, B);
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    for (int b = threadIdx.x; b < B; b += blockDim.x) {
-      if (!selected(mask, b)) continue;
-      if (m.slot[b] < 0) {
-        report(err, SKV_DEV_RING_UNRESERVED);
-        continue;
-      }
-      if (m.pending[b]) {
-        const int c = m.counter[b];
-        m.valid[b] = (c < n_slots ? c : n_slots) * C;
-        m.pending[b] = 0;
-      }
-    }
-  }
+  if (blockIdx.x == 0 && blockIdx.y == 0) ring_commit(m, B, mask, C, n_slots, err);
   const int b = blockIdx.x / spans;
   const int span = blockIdx.x - b * spans;
   if (!selected(mask, b)) return;

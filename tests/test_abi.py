@@ -175,3 +175,29 @@ def test_roll_and_pack_host_errors():
     assert h(P, None, P, None, P, 0, 8, 16, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_SHAPE
     assert h(BAD, None, P, None, P, 2, 8, 16, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_ERR_ALIGN
     assert h(P, None, P, None, P, 2, 0, 16, 1, 64, skv.SKV_BF16, None, None) == skv.SKV_OK  # nothing
+
+
+def test_rope_write_host_errors():
+    f = lib.kv_write_indexed_rope
+    # k_cache, v_cache, k_src, v_src, index, start, B, cap, n, Hkv, D, dtype, inv_freq, layout, err, stream
+    ok = (P, None, P, None, None, 0, 1, 64, 8, 2, 128, skv.SKV_BF16, P, skv.ROPE_HALF, None, None)
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[["kc", "vc", "ks", "vs", "idx", "start", "B", "cap", "n", "Hkv", "D", "dt", "freq",
+               "layout", "err", "st"].index(k)] = v
+        return f(*a)
+    assert call(freq=None) == skv.SKV_ERR_NULL
+    assert call(freq=P + 4) == skv.SKV_ERR_ALIGN
+    assert call(layout=2) == skv.SKV_ERR_RANGE
+    assert call(D=96) == skv.SKV_ERR_SHAPE      # not a power of two
+    assert call(D=8) == skv.SKV_ERR_SHAPE       # fewer than 8 pairs
+    assert call(dt=7) == skv.SKV_ERR_DTYPE
+    assert call(kc=None) == skv.SKV_ERR_NULL
+    assert call(vc=P) == skv.SKV_ERR_NULL       # V cache without V source
+    assert call(start=60) == skv.SKV_ERR_RANGE  # rows 60..67 past cap 64
+    assert call(kc=BAD) == skv.SKV_ERR_ALIGN
+    assert call(B=0) == skv.SKV_OK and call(n=0) == skv.SKV_OK
+    g = lib.kv_ring_write_rope
+    # ring, k_src, v_src, inv_freq, layout, mask, err, stream
+    assert g(None, P, None, P, 0, None, None, None) == skv.SKV_ERR_NULL
