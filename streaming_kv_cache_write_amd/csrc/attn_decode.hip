@@ -83,6 +83,7 @@ template <> struct DecMma<f16_t> {
 constexpr int kDecWaves = 4;    // wavefronts per workgroup
 constexpr int kDecTile = 16;    // keys per wavefront tile (one MFMA block of keys)
 constexpr int kDecChunk = kDecWaves * kDecTile;  // keys per workgroup round; splits are whole chunks
+constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecRows = 16;    // query rows per KV head (MFMA block; R <= 16 are used)
 constexpr int kDecMaxSplits = 32;
 constexpr float kDecRescaleLog2 = 8.f;
@@ -197,16 +198,17 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, int R
   constexpr int kMB = 16;  // o loads in flight per thread
   const int R = a.Tq * group, rows = 4 * RQ;
   const float c2 = a.scale_log2;
+  constexpr int NQ = (kDecRows * 32 + kDecThreads - 1) / kDecThreads;  // (row, split) rounds
   const int pairs = RQ * D;  // (row quad, column)
-  const int tpp = pairs <= 64 ? 4 : pairs <= 128 ? 2 : 1;
+  const int tpp = 4 * pairs <= kDecThreads ? 4 : 2 * pairs <= kDecThreads ? 2 : 1;
   const int t = threadIdx.x, sub = t & (tpp - 1), p0 = t / tpp;
-  const int p_step = 256 / tpp;
+  const int p_step = kDecThreads / tpp;
   const int last_split = n_splits - 1;
 
-  float mm[2], ll[2];  // (m, l) of (row q / 32, split q % 32) for q = t, t + 256
+  float mm[NQ], ll[NQ];  // (m, l) of (row q / 32, split q % 32) for q = t + kDecThreads k
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = t + 256 * k;
+  for (int k = 0; k < NQ; ++k) {
+    const int q = t + kDecThreads * k;
     const size_t base = dec_ml_base(b, g, min(q & 31, last_split), a.Hkv, n_splits);
     const int r = min(q >> 5, rows - 1);
     mm[k] = load_coherent1(rml, base + r);
@@ -224,8 +226,8 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, int R
   load_batch(p0, sub);
 
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int q = t + 256 * k, r = q >> 5, sp = q & 31;
+  for (int k = 0; k < NQ; ++k) {
+    const int q = t + kDecThreads * k, r = q >> 5, sp = q & 31;
     const bool ok = r < rows && sp < n_splits;
     // a clamped split index repeats the row's last split, which leaves the max unchanged;
     // it gets weight 0 (its l, a finite partial of this launch, then adds nothing)
@@ -279,7 +281,7 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, int R
 // reads a cache row another one writes); the last (b, g) to finish sets *cursor = c+Tq and
 // kv_len_out[:] = c+Tq, after every wavefront has read the cursor.
 template <typename T, int D, typename OutT, bool FUSED>
-__global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int group, float* ws,
+__global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int group, float* ws,
                                                                 int n_splits) {
   // P V in fp16 (V converted while staged) for bf16 inputs with an fp32 output, where a
   // bf16-rounded P would be the dominant error of the result
@@ -510,7 +512,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) k_attn_decode(AttnArgs a, int 
   // merge the wavefronts: thread -> (row quad, column)
   const __amdgpu_buffer_rsrc_t ro = ws_rsrc(ws_o, dec_o_floats(a.B, a.Hkv, D, n_splits));
   const __amdgpu_buffer_rsrc_t rml = ws_rsrc(ws_ml, dec_ml_floats(a.B, a.Hkv, n_splits));
-  for (int p = threadIdx.x; p < RQ * D; p += 64 * kDecWaves) {
+  for (int p = threadIdx.x; p < RQ * D; p += kDecThreads) {
     const int rq = p / D, col = p - rq * D;
     float4 mw[kDecWaves], lw[kDecWaves], ow[kDecWaves];
 #pragma unroll
@@ -621,7 +623,7 @@ static hipError_t launch_decode_f(const AttnArgs& a, int group, float* ws, int n
                                   hipStream_t s) {
   const int64_t blocks = (int64_t)n_splits * a.B * a.Hkv;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)blocks), block(64 * kDecWaves);
+  dim3 grid((unsigned)blocks), block(kDecThreads);
   hipLaunchKernelGGL((k_attn_decode<T, D, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
   return hipGetLastError();
 }
