@@ -32,7 +32,8 @@
 //     offset is an immediate and the compiler sees that a load into one buffer cannot alias
 //     reads of the other.
 //   * Workgroup ids are remapped so the query tiles of one (b, h) run on the same XCD and
-//     share its L2 copy of K/V (dispatch hands consecutive workgroup ids to the 8 XCDs in turn).
+//     share its L2 copy of K/V (dispatch hands consecutive workgroup ids to the 8 XCDs in turn),
+//     with the (b, h) pairs dealt round-robin over the XCDs so unequal heads stay balanced.
 #include <type_traits>
 
 #include "common.h"
@@ -141,12 +142,22 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   auto sk = [](int r) { return (r / RP256) % GPR; };
   auto sv = [](int r) { return 4 * ((r / RP256) % (GPR / 4)); };
 
-  // workgroup -> (query tile, head, batch element); tiles of one head stay on one XCD
-  const int nb = gridDim.x, bid = blockIdx.x;
-  const int full = nb & ~7;
-  const int logical = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
-  const int qt = logical % n_qtiles;
-  const int bh = logical / n_qtiles;
+  // workgroup -> (query tile, head, batch element). Dispatch deals consecutive workgroup ids
+  // to the 8 XCDs in turn; the (b, h) pairs are dealt to the XCDs the same way (XCD x takes
+  // bh = x, x + 8, ...), each with all its query tiles in order, so a head's K/V is shared in
+  // one L2 and heads of unequal cost (ragged batch elements) spread over every XCD.
+  const int bid = blockIdx.x, BH = a.B * a.Hq;
+  int qt, bh;
+  if ((BH & 7) == 0) {
+    const int k = bid >> 3, hl = k / n_qtiles;
+    qt = k - hl * n_qtiles;
+    bh = (bid & 7) + 8 * hl;
+  } else {  // contiguous ranges of the (bh, qt) order per XCD
+    const int full = gridDim.x & ~7;
+    const int logical = bid < full ? (bid & 7) * (full >> 3) + (bid >> 3) : bid;
+    qt = logical % n_qtiles;
+    bh = logical / n_qtiles;
+  }
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int g = h / (a.Hq / a.Hkv);
@@ -157,16 +168,9 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   const bool q_ok = my_q < a.Tq;
   OutT* out_row = (OutT*)a.out + (((int64_t)b * a.Tq + my_q) * a.Hq + h) * D;
 
-  const KeySet ks = key_set(a, b);
-  if (!ks.ok) {  // uniform over the workgroup
-    if (q_ok)
-      for (int d = 4 * hi; d < D; d += 8) store4<OutT>(out_row + d, 0.f, 0.f, 0.f, 0.f);
-    if (q_ok && a.lse && hi == 0) a.lse[((int64_t)b * a.Hq + h) * a.Tq + my_q] = -INFINITY;
-    if (tid == 0 && qt == 0 && h == 0) report(a.err, dev_error_bit(a));
-    return;
-  }
-
-  // this wave's queries as the B operand of S^T = K Q^T (loaded once)
+  // this wave's queries as the B operand of S^T = K Q^T (loaded once; they need no key
+  // metadata, so they go out first and their latency overlaps the metadata read and the
+  // first K/V loads -- one wait, after the prologue, covers them all)
   vec qreg[DC];
   {
     const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + my_q) * a.Hq + h) * D + 8 * hi;
@@ -175,10 +179,15 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
       if (q_ok) qreg[c] = *(const vec*)(qp + 16 * c);
       else qreg[c] = vec{};
     }
-    // Wait for these loads here, on every path. Otherwise the compiler may still count them as
-    // outstanding at the head of the tile loop and wait there for all loads -- including the
-    // next tiles', issued one step earlier to hide their latency.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+
+  const KeySet ks = key_set(a, b);
+  if (!ks.ok) {  // uniform over the workgroup
+    if (q_ok)
+      for (int d = 4 * hi; d < D; d += 8) store4<OutT>(out_row + d, 0.f, 0.f, 0.f, 0.f);
+    if (q_ok && a.lse && hi == 0) a.lse[((int64_t)b * a.Hq + h) * a.Tq + my_q] = -INFINITY;
+    if (tid == 0 && qt == 0 && h == 0) report(a.err, dev_error_bit(a));
+    return;
   }
 
   // key range: the workgroup's last query bounds it; keys below key_full are visible to
@@ -397,6 +406,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
     qk(0, sacc[0]);
     __syncthreads();  // every wave has read Ks[0] before tile 0's step refills it
   }
+  // Q's loads are complete on every path from here (the prologue waited for them), so the
+  // compiler counts nothing outstanding at the head of the tile loop, where a wait would
+  // also cover the next tiles' loads
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   int j = 0;
   for (; j + 2 <= n_tiles; j += 2) {
     step(j, std::integral_constant<int, 0>{});
