@@ -100,6 +100,32 @@ def make_flush(torch, dev):
     return lambda: buf.sum()
 
 
+def graph_us_each(torch, fns, replays=4):
+    """Mean GPU time (us) per call of the callables fns, run back to back once each inside one
+    HIP graph (replayed `replays` times, the first untimed). Each call gets its own buffers, more
+    bytes in all than L2 plus the Infinity Cache hold, so every call starts cold without a flush
+    between calls (and without an event pair's dispatch latency around each call)."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for f in fns:
+                f()
+        times = []
+        for _ in range(replays):
+            a, b = event_pair(torch)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+    torch.cuda.synchronize()
+    return statistics.median(times[1:]) * 1e3 / len(fns)
+
+
 # ----------------------------------------------------------------------------------------
 # headline: decode job
 # ----------------------------------------------------------------------------------------
@@ -329,6 +355,18 @@ def bench_ring(torch, skv, SI, dev):
 
     unfused_ms = time_gpu(torch, unfused_rope_write, reps=10, flush=flush)
     del flush
+    # the same write back to back on 6 distinct rings and sources (6 x 115 MB, > L2 + MALL)
+    extra = [skv.Ring(torch.empty_like(ks), torch.empty_like(vs), W.C, W.n_slots, W.sink) for _ in range(6)]
+    esrc = [(SI.per_batch_device_normal(W.B, shape, "ring", "k", dev, "bf16", chunk=2 + i),
+             SI.per_batch_device_normal(W.B, shape, "ring", "v", dev, "bf16", chunk=2 + i)) for i in range(6)]
+    for r in extra:
+        r.reserve()
+    write_b2b_us = graph_us_each(torch, [lambda r=r, e=e: r.write(e[0], e[1]) for r, e in zip(extra, esrc)])
+    rope_b2b_us = graph_us_each(torch, [lambda r=r, e=e: r.write_rope(e[0], e[1], inv)
+                                        for r, e in zip(extra, esrc)])
+    for r in extra:
+        r.close()
+    del extra, esrc
     reset_ms = time_gpu(torch, lambda: ring.reset(), reps=10)
     flop_sat = 4 * W.D * W.H * W.B * W.C * (W.n_slots * W.C)
     flop_seq = sum(4 * W.D * W.H * W.B * W.C * (min(c + 1, W.n_slots) * W.C) * W.rewrites
@@ -345,6 +383,9 @@ def bench_ring(torch, skv, SI, dev):
         "saturated_attn_frac_mfma": flop_sat / attn_ms * 1e-9 / MFMA_BF16_PEAK_TFS,
         "ring_write_ms_cold": write_ms, "ring_write_gbs": wbytes / write_ms * 1e-6,
         "ring_write_frac_hbm": wbytes / write_ms * 1e-6 / HBM_PEAK_GBS,
+        "ring_write_us_back_to_back": write_b2b_us,
+        "ring_write_gbs_back_to_back": wbytes / write_b2b_us * 1e-3,
+        "ring_write_frac_hbm_back_to_back": wbytes / write_b2b_us * 1e-3 / HBM_PEAK_GBS,
         "reset_us": reset_ms * 1e3,
         "rope_write": {
             "what": "kv_ring_write_rope: K rotated at chunk_id*C+t (fp64) as it is written, V copied; "
@@ -352,6 +393,7 @@ def bench_ring(torch, skv, SI, dev):
             "fused_ms_cold": rope_ms, "fused_gbs": wbytes / rope_ms * 1e-6,
             "fused_frac_hbm": wbytes / rope_ms * 1e-6 / HBM_PEAK_GBS,
             "unfused_ms_cold": unfused_ms, "unfused_vs_fused": unfused_ms / rope_ms,
+            "fused_us_back_to_back": rope_b2b_us, "fused_gbs_back_to_back": wbytes / rope_b2b_us * 1e-3,
             "vs_plain_write": rope_ms / write_ms},
         "rolling_arm": {
             "what": "chronological buffer with roll-left past the sink (the path the ring replaces): "
@@ -459,11 +501,21 @@ def bench_sweep(torch, skv, SI, dev):
                      dtype=torch.uint8, device=dev)  # the largest split count of the sweep
     flush = make_flush(torch, dev)
     res = {"workload": "decode attention alone, B=1, 32/8 heads, D=128, bf16, cold L2 and Infinity Cache"}
+    res["method"] = ("us: one launch between an event pair after a 1 GiB read (includes the event "
+                     "pair's dispatch latency); us_back_to_back: launches on distinct caches of "
+                     "capacity kv_len (together > 600 MB, so each starts cold) back to back in a HIP graph")
     for L in (1258, 4096, 8192, 16384, 32768):
         ms = time_gpu(torch, lambda: skv.attn_chunk_fwd(q, kc, vc, out, kv_len=L, workspace=ws), reps=10,
                       flush=flush)
         byts = 2 * L * W.Hkv * W.D * ELEM + 2 * W.Hq * W.D * ELEM
-        res[str(L)] = {"us": ms * 1e3, "gbs": byts / ms * 1e-6, "frac_hbm": byts / ms * 1e-6 / HBM_PEAK_GBS}
+        n_sets = max(6, -(-600_000_000 // byts))
+        caches = [(kc[:, :L].clone(), vc[:, :L].clone()) for _ in range(n_sets)]
+        b2b = graph_us_each(torch, [lambda c=c: skv.attn_chunk_fwd(q, c[0], c[1], out, kv_len=L, workspace=ws)
+                                    for c in caches])
+        del caches
+        res[str(L)] = {"us": ms * 1e3, "gbs": byts / ms * 1e-6, "frac_hbm": byts / ms * 1e-6 / HBM_PEAK_GBS,
+                       "us_back_to_back": b2b, "gbs_back_to_back": byts / b2b * 1e-3,
+                       "frac_hbm_back_to_back": byts / b2b * 1e-3 / HBM_PEAK_GBS}
     ms = time_gpu(torch, lambda: skv.attn_chunk_fwd(q, kc, vc, out, kv_len=1258, full_capacity_masked=True,
                                                     workspace=ws), reps=10, flush=flush)
     byts = 2 * W.cap * W.Hkv * W.D * ELEM
