@@ -299,6 +299,11 @@ def bench_ring(torch, skv, SI, dev):
              SI.per_batch_device_normal(W.B, shape, "ring", "v", dev, "bf16", chunk=c, rewrite=r))
             for c in range(2) for r in range(2)]
     out = torch.empty(W.B, W.C, W.H, W.D, dtype=torch.bfloat16, device=dev)
+    # workspace for the tail split of the attention grid (37 query tiles x 24 heads leave the
+    # second round of workgroups 73% full; its items run as key-range pieces)
+    ws = torch.zeros(max(16, skv.attn_workspace_bytes(srcs[0][0], ks, kv_len_dev=ring.kv_len,
+                                                      max_seqlen_kv=rows)), dtype=torch.uint8, device=dev)
+    no_ws = torch.zeros(16, dtype=torch.uint8, device=dev)  # too small: every item runs whole
 
     def sequence():
         ring.reset()
@@ -307,7 +312,7 @@ def bench_ring(torch, skv, SI, dev):
             for r in range(W.rewrites):
                 q, k, v = srcs[(c % 2) * 2 + (r % 2)]
                 ring.write(k, v)
-                skv.attn_chunk_fwd(q, ks, vs, out, kv_len_dev=ring.kv_len, max_seqlen_kv=rows)
+                skv.attn_chunk_fwd(q, ks, vs, out, kv_len_dev=ring.kv_len, max_seqlen_kv=rows, workspace=ws)
 
     seq_ms = time_gpu(torch, sequence, reps=3, warm=1)
 
@@ -323,7 +328,7 @@ def bench_ring(torch, skv, SI, dev):
             for r in range(W.rewrites):
                 q, k, v = srcs[(c % 2) * 2 + (r % 2)]
                 skv.kv_write_indexed(ks, vs, k, v, start=filled - W.C)
-                skv.attn_chunk_fwd(q, ks, vs, out, kv_len=filled)
+                skv.attn_chunk_fwd(q, ks, vs, out, kv_len=filled, workspace=ws)
 
     roll_seq_ms = time_gpu(torch, rolling_sequence, reps=3, warm=1)
     # saturated step: 7 valid slots
@@ -333,7 +338,9 @@ def bench_ring(torch, skv, SI, dev):
         ring.write(srcs[0][1], srcs[0][2])
     q = srcs[1][0]
     attn_ms = time_gpu(torch, lambda: skv.attn_chunk_fwd(q, ks, vs, out, kv_len_dev=ring.kv_len,
-                                                         max_seqlen_kv=rows), reps=10)
+                                                         max_seqlen_kv=rows, workspace=ws), reps=10)
+    attn_whole_ms = time_gpu(torch, lambda: skv.attn_chunk_fwd(q, ks, vs, out, kv_len_dev=ring.kv_len,
+                                                               max_seqlen_kv=rows, workspace=no_ws), reps=10)
     flush = make_flush(torch, dev)
     write_ms = time_gpu(torch, lambda: ring.write(srcs[0][1], srcs[0][2]), reps=10, flush=flush)
     roll_ms = time_gpu(torch, lambda: skv.kv_roll_left(ks, vs, W.sink * W.C, W.C), reps=10, flush=flush)
@@ -381,6 +388,9 @@ def bench_ring(torch, skv, SI, dev):
         "ms_per_rewrite_step": seq_ms / (W.n_chunks * W.rewrites),
         "saturated_attn_ms": attn_ms, "saturated_attn_tflops": flop_sat / attn_ms * 1e-9,
         "saturated_attn_frac_mfma": flop_sat / attn_ms * 1e-9 / MFMA_BF16_PEAK_TFS,
+        "saturated_attn_tail_split_workspace_mb": ws.numel() / 1e6,
+        "saturated_attn_whole_items_ms": attn_whole_ms,
+        "saturated_attn_whole_items_tflops": flop_sat / attn_whole_ms * 1e-9,
         "ring_write_ms_cold": write_ms, "ring_write_gbs": wbytes / write_ms * 1e-6,
         "ring_write_frac_hbm": wbytes / write_ms * 1e-6 / HBM_PEAK_GBS,
         "ring_write_us_back_to_back": write_b2b_us,

@@ -233,15 +233,21 @@ skv_status kv_pack_ragged(void* k_packed, void* v_packed, const void* k_padded, 
  * exp(scale*score). scale == 0 means 1/sqrt(D). D in {64, 128}.
  * dtype: SKV_F32 (exact fp32 arithmetic), SKV_BF16 or SKV_F16 (matrix-core products with
  * fp32 accumulation and fp32 softmax). out_dtype: dtype or SKV_F32.
- * Tq <= 4 (decode-sized chunks) in bf16/f16 uses a split-K path that needs a workspace of
- * attn_workspace_bytes(params) bytes (caller device memory, 16-byte aligned); other shapes
- * need none. The workspace must be zero-filled once before its first use: its first bytes
- * hold arrival counters (B*Hkv + 1 int32, at offset 0 whatever the split count) that every call
- * leaves at zero again, so one zero-filled workspace of the largest size needed can serve
- * every later call. Calls sharing one workspace must not overlap in time (they are ordered
- * when issued on one stream).
+ * Workspace (caller device memory, 16-byte aligned, attn_workspace_bytes(params) bytes):
+ *   - Tq <= 4 (decode-sized chunks) in bf16/f16 uses a split-K path that requires it;
+ *   - larger bf16/f16 chunks take it optionally: when attn_workspace_bytes() is nonzero for
+ *     them, the last, partly filled round of workgroups would leave CU slots idle, and a
+ *     workspace of that size lets the kernel cut that round's items into key-range pieces
+ *     merged in the same launch. Without one (NULL or smaller) every item runs whole; the
+ *     results agree up to the order of the final sums;
+ *   - fp32 needs none.
+ * The workspace must be zero-filled once before its first use: its first bytes hold arrival
+ * counters (int32, at offset 0) that every call leaves at zero again, so one zero-filled
+ * workspace of the largest size needed can serve every later call. Calls sharing one
+ * workspace must not overlap in time (they are ordered when issued on one stream).
  * max_seqlen_kv: optional host bound on any batch element's key count; it only sizes the
- * split-K grid when the lengths live on the device (0 = use cap / the host kv_len).
+ * split grids and the workspace when the lengths live on the device (0 = use cap / the host
+ * kv_len).
  * ------------------------------------------------------------------------------------ */
 typedef enum {
   SKV_MASK_NONE = 0,

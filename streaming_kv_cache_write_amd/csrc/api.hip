@@ -28,7 +28,8 @@ hipError_t launch_ring_write_rope(const void*, const void*, void*, void*, int32_
                                   const uint8_t*, int, int, int, int, int, const double*, int,
                                   int32_t*, hipStream_t);
 hipError_t launch_attn_f32(const AttnArgs&, int, hipStream_t);
-hipError_t launch_attn_flash(const AttnArgs&, int, int, int, hipStream_t);
+hipError_t launch_attn_flash(const AttnArgs&, int, int, int, int, void*, size_t, hipStream_t);
+size_t flash_workspace_bytes(int B, int Hq, int Tq, int D, int key_bound);
 hipError_t launch_attn_decode(const AttnArgs&, int, int, int, void*, int, hipStream_t);
 int decode_splits(int B, int Hkv, int max_len);
 size_t decode_workspace_bytes(int B, int Hkv, int D, int n_splits);
@@ -83,7 +84,8 @@ Path choose_path(const skv_attn_params& p) {
   return PATH_FLASH;
 }
 
-int decode_max_len(const skv_attn_params& p) {
+// Host bound on the keys any batch element attends to (sizes split grids and workspaces).
+int key_bound(const skv_attn_params& p) {
   if (p.flags & SKV_FULL_CAPACITY_MASKED) return p.cap;
   if (p.cu_seqlens_kv_dev || p.kv_len_dev)
     return p.max_seqlen_kv > 0 ? (p.max_seqlen_kv < p.cap ? p.max_seqlen_kv : p.cap) : p.cap;
@@ -355,8 +357,9 @@ skv_status kv_pack_ragged(void* k_packed, void* v_packed, const void* k_padded, 
 
 size_t attn_workspace_bytes(const skv_attn_params* p) {
   if (!p || validate_attn((void*)16, (void*)16, (void*)16, (void*)16, p) != SKV_OK) return 0;
-  if (choose_path(*p) != PATH_DECODE) return 0;
-  const int splits = decode_splits(p->B, p->Hkv, decode_max_len(*p));
+  if (choose_path(*p) == PATH_F32) return 0;
+  if (choose_path(*p) == PATH_FLASH) return flash_workspace_bytes(p->B, p->Hq, p->Tq, p->D, key_bound(*p));
+  const int splits = decode_splits(p->B, p->Hkv, key_bound(*p));
   return decode_workspace_bytes(p->B, p->Hkv, p->D, splits);
 }
 
@@ -391,10 +394,11 @@ skv_status attn_chunk_fwd(const void* q, const void* k, const void* v, void* out
     case PATH_F32:
       return hip_status(launch_attn_f32(a, p->D, s), "attn_chunk_fwd (fp32) launch");
     case PATH_FLASH:
-      return hip_status(launch_attn_flash(a, p->dtype, p->out_dtype, p->D, s),
+      return hip_status(launch_attn_flash(a, p->dtype, p->out_dtype, p->D, key_bound(*p),
+                                          p->workspace, p->workspace_bytes, s),
                         "attn_chunk_fwd (flash) launch");
     case PATH_DECODE: {
-      const int splits = decode_splits(p->B, p->Hkv, decode_max_len(*p));
+      const int splits = decode_splits(p->B, p->Hkv, key_bound(*p));
       const size_t need = decode_workspace_bytes(p->B, p->Hkv, p->D, splits);
       if (!p->workspace) return fail(SKV_ERR_NULL, "decode-sized call needs a workspace of %zu bytes", need);
       if (p->workspace_bytes < need)

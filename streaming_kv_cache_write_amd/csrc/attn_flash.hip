@@ -34,6 +34,10 @@
 //   * Workgroup ids are remapped so the query tiles of one (b, h) run on the same XCD and
 //     share its L2 copy of K/V (dispatch hands consecutive workgroup ids to the 8 XCDs in turn),
 //     with the (b, h) pairs dealt round-robin over the XCDs so unequal heads stay balanced.
+//   * Tail split (optional, needs a workspace): when the last round of workgroups would leave
+//     many of the CU slots idle, the items of that round are cut by key range into a few
+//     pieces. Each piece stores its unnormalised O^T, reference max and row sums; the last
+//     piece of an item to finish (an arrival count) merges them and writes the output.
 #include <type_traits>
 
 #include "common.h"
@@ -108,12 +112,35 @@ template <> __device__ __forceinline__ void store4<f16_t>(f16_t* p, float a, flo
 
 constexpr int kFlashBM = 128;  // queries per workgroup
 constexpr int kFlashBN = 64;   // keys per tile
+constexpr int kFlashSlotsPerXcd = 64;  // 32 CUs x 2 resident workgroups
+constexpr int kFlashMinPieceTiles = 16;  // a key-range piece covers at least this many tiles
+
+// Which item (query tile, b, h) and key-range piece a workgroup runs. With the (b, h) pairs
+// dealt evenly over the 8 XCDs each XCD runs items 0 .. nf + r - 1 of its own; items below nf
+// run whole, the last r are each cut into `parts` key-range pieces (part-major order, so the
+// pieces that read the same keys run together). parts == 1: no split (nf and r unused).
+struct FlashGrid {
+  int n_qtiles;
+  int nf, r, parts;
+  float* ws;  // parts > 1: arrival counters, then the pieces' partials
+};
+
+// Workspace of the tail split: int32 arrival counters (one per split item, left at zero by
+// every launch), padded to 256 bytes, then per (split item, piece) a block of 256 lanes x
+// (D/2 floats of O^T + the reference max + the row sum), lane-interleaved.
+__host__ __device__ constexpr int flash_piece_floats(int D) { return 256 * (D / 2 + 2); }
+__host__ __device__ constexpr int flash_counter_floats(int n_split) { return (n_split + 63) & ~63; }
+
+// Device-coherent (sc1) buffer accesses, as agent-scope atomic stores and loads take: the
+// pieces of one item run on one XCD, but nothing ties a later launch reusing the workspace to
+// that XCD, so the partials bypass the per-XCD L2 state the same way the decode merge does.
+constexpr int kFlashCoherent = 16;
 
 // PV16: run P V in fp16 (P rounded to fp16, V converted bf16 -> fp16 in LDS after it lands)
 // instead of the input type. Used for bf16 inputs with an fp32 output, where bf16-rounded P
 // would be the dominant error of the result.
 template <typename T, int D, typename OutT, bool PV16>
-__global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles) {
+__global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg) {
   typedef typename Mfma<T>::vec vec;
   typedef typename std::conditional<PV16, f16_t, T>::type TV;  // type of V and P in P V
   typedef typename Mfma<TV>::vec vecv;
@@ -146,10 +173,18 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   // to the 8 XCDs in turn; the (b, h) pairs are dealt to the XCDs the same way (XCD x takes
   // bh = x, x + 8, ...), each with all its query tiles in order, so a head's K/V is shared in
   // one L2 and heads of unequal cost (ragged batch elements) spread over every XCD.
-  const int bid = blockIdx.x, BH = a.B * a.Hq;
-  int qt, bh;
+  const int bid = blockIdx.x, BH = a.B * a.Hq, n_qtiles = fg.n_qtiles;
+  int qt, bh, part = 0, split_id = -1;
   if ((BH & 7) == 0) {
-    const int k = bid >> 3, hl = k / n_qtiles;
+    int k = bid >> 3;
+    if (fg.parts > 1 && k >= fg.nf) {  // piece `part` of item nf + ri
+      const int u = k - fg.nf;
+      part = u / fg.r;
+      const int ri = u - part * fg.r;
+      split_id = (bid & 7) * fg.r + ri;
+      k = fg.nf + ri;
+    }
+    const int hl = k / n_qtiles;
     qt = k - hl * n_qtiles;
     bh = (bid & 7) + 8 * hl;
   } else {  // contiguous ranges of the (bh, qt) order per XCD
@@ -197,14 +232,25 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   const int shift = ks.len - a.Tq;  // query t sits at absolute position t + shift
   const int key_end = a.full_cap ? ks.visit : row_limit(a.mask, a.block, q_last + shift, ks.len) + 1;
   const int key_full = row_limit(a.mask, a.block, q_first + shift, ks.len) + 1;
-  const int my_lim = row_limit(a.mask, a.block, my_q + shift, ks.len);  // last key this row sees
-  const int n_tiles = (key_end + BN - 1) / BN;
-  const int n_full = min(key_end, (key_full / BN) * BN) / BN;
+  int my_lim = row_limit(a.mask, a.block, my_q + shift, ks.len);  // last key this row sees
+  int n_tiles = (key_end + BN - 1) / BN;
+  int n_full = min(key_end, (key_full / BN) * BN) / BN;
 
   const int64_t rstride = (int64_t)a.Hkv * D;
   const T* kbase = (const T*)a.k + ks.base_row * rstride + (int64_t)g * D;
   const T* vbase = (const T*)a.v + ks.base_row * rstride + (int64_t)g * D;
   const int row_bytes = (int)(rstride * sizeof(T));
+  int visit = ks.visit;  // rows from the tile base that exist
+  if (split_id >= 0) {
+    // this piece's tiles [t0, t1): everything below is re-based to tile t0
+    const int t0 = part * n_tiles / fg.parts, t1 = (part + 1) * n_tiles / fg.parts;
+    kbase += (int64_t)t0 * BN * rstride;
+    vbase += (int64_t)t0 * BN * rstride;
+    visit -= t0 * BN;
+    my_lim -= t0 * BN;
+    n_full = min(max(n_full - t0, 0), t1 - t0);
+    n_tiles = t1 - t0;
+  }
 
   // Direct loads: piece c = wave * CPW + i of a tile covers rows [c * RPC, +RPC); lane L fills
   // LDS bytes [c * 1024 + 16 L, +16), i.e. row c * RPC + L / GPR at position L % GPR, and so
@@ -219,7 +265,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
     voff[i] = (uint32_t)(r * row_bytes + 16 * (p ^ sv(r)));
   }
   auto dma = [&](const T* base, int tile, unsigned char* dst, const uint32_t* off) {
-    const int rows = min(ks.visit - tile, BN);
+    const int rows = min(visit - tile, BN);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(base + (int64_t)tile * rstride), (short)0, rows * row_bytes, kBufferRsrcWord3);
 #pragma unroll
@@ -417,6 +463,74 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   }
   if (j < n_tiles) step(j, std::integral_constant<int, 0>{});
 
+  if (split_id >= 0) {
+    // Store this piece's partial; the last piece of the item to arrive merges all of them.
+    const int PF = flash_piece_floats(D);
+    float* const blocks = fg.ws + flash_counter_floats(8 * fg.r) + (size_t)split_id * fg.parts * PF;
+    auto rsrc = [&](int p) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(blocks + (size_t)p * PF), (short)0,
+                                               PF * (int)sizeof(float), kBufferRsrcWord3);
+    };
+    // float offset of lane data: O^T group gi (db = gi / 4, rows 4i .. 4i+3 of the 16) as one
+    // float4 per lane, then the max and the row sum
+    auto o_off = [&](int gi) { return ((gi * 4 + wave) * 64 + lane) * 4; };
+    const int ml_off = 256 * (D / 2) + wave * 128 + lane;
+    {
+      const auto r = rsrc(part);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 d = {__float_as_uint(o[db][4 * i]), __float_as_uint(o[db][4 * i + 1]),
+                           __float_as_uint(o[db][4 * i + 2]), __float_as_uint(o[db][4 * i + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(d, r, 4 * o_off(4 * db + i), 0, kFlashCoherent);
+        }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), r, 4 * ml_off, 0, kFlashCoherent);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lsum), r, 4 * (ml_off + 64), 0,
+                                            kFlashCoherent);
+    }
+    // every store of the workgroup has completed before its arrival is counted
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    volatile int* last_flag = (volatile int*)Ks0;  // LDS is idle after the tile loop
+    if (tid == 0) {
+      int* cnt = (int*)fg.ws + split_id;
+      const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == fg.parts - 1;
+      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *last_flag = last;
+    }
+    __syncthreads();
+    if (!*last_flag) return;
+    // the sc1 loads see every store that completed before its piece was counted; the fence
+    // keeps the compiler from hoisting them above the count
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    for (int p = 0; p < fg.parts; ++p) {
+      if (p == part) continue;
+      const auto r = rsrc(p);
+      const float mp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * ml_off, 0, kFlashCoherent));
+      const float lp =
+          __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * (ml_off + 64), 0, kFlashCoherent));
+      u32x4 op[4 * DB];
+#pragma unroll
+      for (int gi = 0; gi < 4 * DB; ++gi)
+        op[gi] = __builtin_amdgcn_raw_buffer_load_b128(r, 4 * o_off(gi), 0, kFlashCoherent);
+      // rescale both sides to the larger reference (an empty piece has m = -inf, l = 0, O = 0)
+      const float mn = fmaxf(m, mp);
+      const float base = mn == -INFINITY ? 0.f : mn;
+      const float wa = fast_exp2((m - base) * c), wb = fast_exp2((mp - base) * c);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[db][4 * i + e] = o[db][4 * i + e] * wa + __uint_as_float(op[4 * db + i][e]) * wb;
+      lsum = lsum * wa + lp * wb;
+      m = mn;
+    }
+  }
+
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (q_ok) {
@@ -435,26 +549,77 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, int n_qtiles)
   }
 }
 
+// Tail split plan. Each XCD holds kFlashSlotsPerXcd workgroups at a time; with I items per
+// XCD, F = I / slots whole rounds and R = I % slots items left, the last round leaves slots
+// idle. Cutting those R items into k key-range pieces makes that round ceil(R k / slots) / k
+// of an item's time instead of one. k is the smallest that minimises it, and the split is
+// used only if it saves at least 5% and every piece keeps kFlashMinPieceTiles tiles at the
+// host's bound on the key count.
+struct FlashPlan {
+  int n_qtiles, nf, r, parts;
+};
+static FlashPlan flash_plan(int B, int Hq, int Tq, int key_bound) {
+  FlashPlan pl{(Tq + kFlashBM - 1) / kFlashBM, 0, 0, 1};
+  const int64_t BH = (int64_t)B * Hq;
+  const int64_t items = (int64_t)pl.n_qtiles * BH;
+  if (BH % 8 != 0 || items > 0x7fffffff) return pl;
+  const int I = (int)(items / 8);
+  pl.nf = I;
+  const int F = I / kFlashSlotsPerXcd, R = I % kFlashSlotsPerXcd;
+  if (F == 0 || R == 0) return pl;
+  double best = F + 1.0;
+  int best_k = 1;
+  for (int k = 2; k <= 8; ++k) {
+    if ((int64_t)key_bound < (int64_t)k * kFlashMinPieceTiles * kFlashBN) break;
+    const double cost = F + (double)((R * k + kFlashSlotsPerXcd - 1) / kFlashSlotsPerXcd) / k;
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_k = k;
+    }
+  }
+  if (best_k == 1 || best > 0.95 * (F + 1)) return pl;
+  pl.nf = I - R;
+  pl.r = R;
+  pl.parts = best_k;
+  return pl;
+}
+
+size_t flash_workspace_bytes(int B, int Hq, int Tq, int D, int key_bound) {
+  const FlashPlan pl = flash_plan(B, Hq, Tq, key_bound);
+  if (pl.parts == 1) return 0;
+  const size_t n_split = (size_t)8 * pl.r;
+  return ((size_t)flash_counter_floats((int)n_split) + n_split * pl.parts * flash_piece_floats(D)) *
+         sizeof(float);
+}
+
 template <typename T, typename OutT>
-static hipError_t launch_flash_t(const AttnArgs& a, int D, hipStream_t s) {
+static hipError_t launch_flash_t(const AttnArgs& a, int D, FlashGrid fg, hipStream_t s) {
   constexpr bool kPV16 = std::is_same<T, bf16_t>::value && std::is_same<OutT, float>::value;
-  const int n_qtiles = (a.Tq + kFlashBM - 1) / kFlashBM;
-  const int64_t blocks = (int64_t)n_qtiles * a.Hq * a.B;
+  const int64_t blocks = fg.parts == 1 ? (int64_t)fg.n_qtiles * a.Hq * a.B
+                                       : (int64_t)8 * (fg.nf + fg.r * fg.parts);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks), block(256);
   if (D == 128)
-    hipLaunchKernelGGL((k_attn_flash<T, 128, OutT, kPV16>), grid, block, 0, s, a, n_qtiles);
+    hipLaunchKernelGGL((k_attn_flash<T, 128, OutT, kPV16>), grid, block, 0, s, a, fg);
   else
-    hipLaunchKernelGGL((k_attn_flash<T, 64, OutT, kPV16>), grid, block, 0, s, a, n_qtiles);
+    hipLaunchKernelGGL((k_attn_flash<T, 64, OutT, kPV16>), grid, block, 0, s, a, fg);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_flash(const AttnArgs& a, int dtype, int out_dtype, int D, hipStream_t s) {
+// ws: the caller's workspace or nullptr. The tail split runs only when the plan asks for one
+// and ws holds flash_workspace_bytes (16-byte aligned, counters zero); otherwise every item
+// runs whole, with the same result up to the order of the final sums.
+hipError_t launch_attn_flash(const AttnArgs& a, int dtype, int out_dtype, int D, int key_bound,
+                             void* ws, size_t ws_bytes, hipStream_t s) {
+  const FlashPlan pl = flash_plan(a.B, a.Hq, a.Tq, key_bound);
+  FlashGrid fg{pl.n_qtiles, pl.nf, pl.r, pl.parts, (float*)ws};
+  const size_t need = flash_workspace_bytes(a.B, a.Hq, a.Tq, D, key_bound);
+  if (pl.parts == 1 || !ws || ws_bytes < need || ((uintptr_t)ws & 15)) fg = FlashGrid{pl.n_qtiles, 0, 0, 1, nullptr};
   if (dtype == SKV_BF16)
-    return out_dtype == SKV_F32 ? launch_flash_t<bf16_t, float>(a, D, s)
-                                : launch_flash_t<bf16_t, bf16_t>(a, D, s);
-  return out_dtype == SKV_F32 ? launch_flash_t<f16_t, float>(a, D, s)
-                              : launch_flash_t<f16_t, f16_t>(a, D, s);
+    return out_dtype == SKV_F32 ? launch_flash_t<bf16_t, float>(a, D, fg, s)
+                                : launch_flash_t<bf16_t, bf16_t>(a, D, fg, s);
+  return out_dtype == SKV_F32 ? launch_flash_t<f16_t, float>(a, D, fg, s)
+                              : launch_flash_t<f16_t, f16_t>(a, D, fg, s);
 }
 
 }  // namespace skv

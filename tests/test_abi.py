@@ -104,6 +104,51 @@ def test_valid_kv_len_bounds_pass_validation_of_workspace_query():
     assert large > small
 
 
+def flash_tail_plan(B, Hq, Tq, key_bound):
+    """The chunk-attention tail split restated: 64 resident workgroups per XCD; with I items
+    per XCD, F whole rounds and R items left, cut those R into the k pieces (2..8, each piece
+    at least 16 tiles of 64 keys at the bound) that minimise F + ceil(R k / 64) / k, if that
+    saves 5% of the F + 1 rounds."""
+    nq = -(-Tq // 128)
+    if (B * Hq) % 8:
+        return 1, 0
+    I = nq * B * Hq // 8
+    F, R = divmod(I, 64)
+    if F == 0 or R == 0:
+        return 1, 0
+    best, bk = F + 1.0, 1
+    for k in range(2, 9):
+        if key_bound < k * 16 * 64:
+            break
+        cost = F + (-(-R * k // 64)) / k
+        if cost < best - 1e-9:
+            best, bk = cost, k
+    return (bk, R) if bk > 1 and best <= 0.95 * (F + 1) else (1, 0)
+
+
+@pytest.mark.parametrize("B,Hq,Tq,kv_len,D", [
+    (2, 12, 4680, 32760, 128),   # ring: 37 query tiles x 24 heads, 111 items per XCD -> 4 pieces
+    (2, 8, 4700, 6500, 128),     # 74 items per XCD, 10 left over -> 6 pieces
+    (2, 8, 4700, 6500, 64),
+    (2, 8, 4700, 5000, 128),     # bound allows 4 pieces only
+    (2, 8, 4700, 1500, 128),     # pieces would be too short: no split
+    (8, 40, 1024, 16384, 128),   # 320 items per XCD = 5 whole rounds: no split
+    (2, 3, 4700, 6500, 128),     # heads do not divide over the XCDs: no split
+    (1, 8, 4700, 6500, 128),     # 37 items per XCD, one round: no split
+])
+def test_flash_tail_split_workspace(B, Hq, Tq, kv_len, D):
+    """attn_workspace_bytes of chunk-sized calls: zero unless the tail split is planned, then
+    the arrival counters (padded to 256 bytes) and one partial of 256 lanes x (D/2 + 2)
+    floats per piece."""
+    k, R = flash_tail_plan(B, Hq, Tq, kv_len)
+    n_split = 8 * R
+    want = 0 if k == 1 else 4 * (((n_split + 63) // 64) * 64 + n_split * k * 256 * (D // 2 + 2))
+    p = params(B=B, Hq=Hq, Hkv=Hq if Hq % 2 else Hq // 2, Tq=Tq, D=D, cap=kv_len, kv_len=kv_len)
+    assert lib.attn_workspace_bytes(ctypes.byref(p)) == want
+    if (B, Hq, Tq) == (2, 12, 4680):
+        assert (k, R) == (4, 47)
+
+
 def test_write_host_errors():
     f = lib.kv_write_indexed
     # k_cache, v_cache, k_src, v_src, index, start, B, cap, n, Hkv, D, dtype, err, stream

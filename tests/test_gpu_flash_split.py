@@ -1,0 +1,155 @@
+"""The chunk-attention tail split against the fp64 oracle: when the last round of workgroups
+would leave most CU slots idle, its items are cut into key-range pieces whose partials the
+last piece to arrive merges. Shapes here are chosen so that the split is planned (B=2, 8
+query heads, 37 query tiles: 74 items per XCD, the last 10 cut into pieces), and the rows
+checked are those of the split items (batch element 1, queries from 3456 on) plus a few
+whole ones. Covered: host and device lengths, lengths so short that most pieces are empty,
+causal masking, packed K/V, the full-capacity arm, fp32 output with the LSE, fp16, D=64,
+and a workspace reused across calls (its arrival counters return to zero)."""
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as SI
+from oracle import attention as A
+from tests.helpers import check_attention, f64
+
+skv = pytest.importorskip("streaming_kv_cache_write_amd")
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+B, TQ, HQ, HKV = 2, 4700, 8, 2
+SPLIT_T0 = 27 * 128  # first query of the split items (query tiles 27..36 of batch element 1)
+
+
+def inputs(D, cap, dtype, seed):
+    q = SI.per_batch_normal(B, (TQ, HQ, D), "misc", "q", chunk=seed, dtype=dtype)
+    k = SI.per_batch_normal(B, (cap, HKV, D), "misc", "k", chunk=seed, dtype=dtype)
+    v = SI.per_batch_normal(B, (cap, HKV, D), "misc", "v", chunk=seed, dtype=dtype)
+    return q, k, v
+
+
+def sample_rows(seed):
+    rng = np.random.default_rng(seed)
+    split = np.unique(np.concatenate([[SPLIT_T0, TQ - 1], rng.integers(SPLIT_T0, TQ, size=300)]))
+    whole = np.unique(np.concatenate([[0], rng.integers(0, SPLIT_T0, size=20)]))
+    return whole, split
+
+
+def oracle_rows(q, kk, vv, ts, L, mask, Lvis=None):
+    """Oracle output of query rows ts (all heads) over key rows [0, Lvis) of which [0, L) are
+    active (Lvis > L only for the full-capacity arm, whose extra rows are masked)."""
+    Lvis = L if Lvis is None else Lvis
+    allowed = np.zeros((len(ts), Lvis), dtype=bool)
+    for i, t in enumerate(ts):
+        allowed[i, :L] = A.visible_keys(int(t), TQ, L, mask)
+    o, lse = A.attend_keys(q[ts], kk[:Lvis], vv[:Lvis], allowed)
+    return o, lse
+
+
+def run(q, k, v, ws, **kw):
+    return skv.attn_chunk_fwd(q, k, v, workspace=ws, **kw)
+
+
+def check_split_call(dtype, D, cap, lens, mask=A.MASK_NONE, mode="host", out_f32=False, seed=0):
+    q, k, v = inputs(D, cap, dtype, seed)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    kw = dict(mask=mask, out_dtype=torch.float32 if out_f32 else None)
+    if mode == "host":
+        assert lens[0] == lens[1]
+        kw["kv_len"] = lens[0]
+    elif mode == "device":
+        kw["kv_len_dev"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        kw["max_seqlen_kv"] = cap
+    elif mode == "full":
+        kw["kv_len_dev"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        kw["full_capacity_masked"] = True
+    elif mode == "packed":
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        kd = torch.cat([kd[b, :lens[b]] for b in range(B)]).contiguous()
+        vd = torch.cat([vd[b, :lens[b]] for b in range(B)]).contiguous()
+        kw["cu_seqlens_kv"] = torch.from_numpy(cu).to(DEV)
+        kw["max_seqlen_kv"] = max(lens)
+    need = skv.attn_workspace_bytes(qd, kd, **kw)
+    assert need > 0, "the tail split is not planned for this shape"
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    lse = torch.empty(B, HQ, TQ, dtype=torch.float32, device=DEV)
+    o = run(qd, kd, vd, ws, lse=lse, **kw)
+    # the same call with a workspace too small for the split runs every item whole
+    o_whole = run(qd, kd, vd, torch.zeros(16, dtype=torch.uint8, device=DEV), **kw)
+    torch.cuda.synchronize()
+    assert not ws[:4 * 8 * 10].any(), "arrival counters not returned to zero"
+
+    whole, split = sample_rows(seed)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    got, want = [], []
+    for b, ts in ((0, whole), (1, whole), (1, split)):
+        L = lens[b]
+        Lvis = cap if mode == "full" else None
+        ref, lse_ref = oracle_rows(qf[b], kf[b], vf[b], ts, L, mask, Lvis)
+        tsd = torch.from_numpy(ts).to(DEV)
+        got.append(f64(o[b, tsd]))
+        want.append(ref)
+        if out_f32:
+            assert np.max(np.abs(f64(lse[b][:, tsd]) - lse_ref)) <= 2e-3
+    check_attention(np.concatenate(got), np.concatenate(want), dtype,
+                    f"split {dtype} D{D} {mode} lens {lens} mask {mask}")
+    # split and whole runs differ only in the order of the final sums
+    diff = (o.float() - o_whole.float()).abs().max().item()
+    assert diff <= (2e-3 if out_f32 else 2e-2), diff
+    return ws
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_split_host_len(dtype):
+    check_split_call(dtype, 128, 8192, [6500, 6500], seed=1)
+
+
+def test_split_device_lens_unequal():
+    check_split_call("bf16", 128, 8192, [6500, 2500], mode="device", seed=2)
+
+
+def test_split_mostly_empty_pieces():
+    # batch element 1 (the split items) has 100 keys: two tiles for six pieces
+    check_split_call("bf16", 128, 8192, [6500, 100], mode="device", seed=3)
+
+
+def test_split_causal():
+    check_split_call("bf16", 128, 8192, [6500, 6500], mask=A.MASK_CAUSAL, seed=4)
+
+
+def test_split_packed():
+    check_split_call("bf16", 128, 6200, [6100, 5000], mode="packed", seed=5)
+
+
+def test_split_full_capacity_arm():
+    check_split_call("bf16", 128, 8192, [3000, 7000], mode="full", seed=6)
+
+
+def test_split_fp32_out_and_lse():
+    check_split_call("bf16", 128, 8192, [6500, 6500], out_f32=True, seed=7)
+
+
+def test_split_d64():
+    check_split_call("bf16", 64, 8192, [7000, 7000], seed=8)
+
+
+def test_split_workspace_reused():
+    """Back-to-back split launches on one workspace with different lengths: every launch
+    merges exactly its own pieces."""
+    dtype, D, cap = "bf16", 128, 8192
+    q, k, v = inputs(D, cap, dtype, 9)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    kl = torch.zeros(B, dtype=torch.int32, device=DEV)
+    need = skv.attn_workspace_bytes(qd, kd, kv_len_dev=kl, max_seqlen_kv=cap)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    whole, split = sample_rows(9)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    for lens in ([8000, 8000], [300, 5000], [8192, 64], [4000, 4100]):
+        kl.copy_(torch.tensor(lens, dtype=torch.int32))
+        o = skv.attn_chunk_fwd(qd, kd, vd, kv_len_dev=kl, max_seqlen_kv=cap, workspace=ws)
+        ref, _ = oracle_rows(qf[1], kf[1], vf[1], split, lens[1], A.MASK_NONE)
+        check_attention(o[1, torch.from_numpy(split).to(DEV)], ref, dtype, f"reuse {lens}")
+    torch.cuda.synchronize()
+    assert not ws[:4 * 8 * 10].any()
