@@ -12,10 +12,13 @@
 // position is its slab row (the write index), or chunk_id * C + t in the ring (chunk_id = the
 // number of chunks reserved before it since reset). V rows are copied unchanged.
 //
-// One thread takes one token row and 8 coordinate pairs (16 elements) of every head: the 8
-// sines and cosines are computed once and reused for all Hkv heads, whose loads go out four
-// heads at a time. The kernels are HBM-bound like the plain writes (each K and V byte read
-// once and written once); the fp64 trig costs 8 sincos per (token, 8 pairs), not per head.
+// A workgroup takes a block of tb consecutive tokens of one batch element (all heads) and one
+// tensor (grid.y: 0 = K, 1 = V). The block is cut into units of (token, head, 8 coordinate
+// pairs = 16 elements); each thread issues the loads of 4 units before anything else. The K
+// workgroups meanwhile compute the fp64 cosine and sine of every (token, pair) of the block
+// once, into LDS, where all heads of the token share them; after one barrier each unit is
+// rotated from its registers and stored. V workgroups copy their units unchanged. The kernels
+// are HBM-bound like the plain writes (each K and V byte read once and written once).
 #include "common.h"
 #include "ring_meta.h"
 
@@ -76,164 +79,231 @@ __device__ __forceinline__ void store8(float* p, const double* x) {
   *(float4*)(p + 4) = make_float4((float)x[4], (float)x[5], (float)x[6], (float)x[7]);
 }
 
-// cos and sin of position * inv_freq[8g + j], j < 8
-__device__ __forceinline__ void rope_angles(int64_t pos, const double* inv_freq, int g, double* c,
-                                            double* s) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) sincos((double)pos * inv_freq[8 * g + j], &s[j], &c[j]);
-}
+constexpr int kRopeUnits = 4;          // units whose loads a thread issues together
+constexpr int kRopeTablePairs = 2048;  // (cos, sin) entries in LDS: 32 KB of fp64
 
-constexpr int kRopeHeadGroup = 4;  // heads whose loads are issued together
+// Token t of the block -> its absolute position and its destination row (element offset of
+// the row in the destination tensor); ok = false: the token is not written.
+struct RopeTok {
+  int64_t pos;
+  int64_t dst_row;
+  bool ok;
+};
 
-// Rotate pairs 8g .. 8g+7 of every head of one token row at position pos. LAYOUT 0: pair
-// i = (i, i + D/2); LAYOUT 1: pair i = (2i, 2i + 1). Heads go in groups of kRopeHeadGroup,
-// alternating between two register buffers: the next group's loads are in flight while a
-// group is rotated and stored (the first group's also while the angles are computed).
-template <typename T, int LAYOUT>
-__device__ __forceinline__ void rope_row(const T* src, T* dst, int Hkv, int D, int g, int64_t pos,
-                                         const double* inv_freq) {
+#ifndef SKV_ROPE_TRIG_FIRST
+#define SKV_ROPE_TRIG_FIRST 1
+#endif
+
+// One workgroup: tokens [t0, t0 + nt) of one batch element. src points at token t0's row;
+// pos_of(t) gives a block-local token's absolute position (it may read memory), place(p, t)
+// its destination and whether it is written (arithmetic only). ROTATE: K (rotate by the
+// LDS table), else V (copy). Units: u -> token u / (Hkv*G), head, group g (G = D/16); pairs
+// 8g .. 8g+7 are elements (8g + j, D/2 + 8g + j) in layout 0 and (16g + 2j, 16g + 2j + 1) in
+// layout 1.
+//
+// Ordering matters here because the hardware counts outstanding loads in issue order: a wait
+// for one load is a wait for every load issued before it. So the frequencies and positions
+// the angle table needs are loaded before any unit, and nothing waits on the unit loads until
+// their rotation. The source and destination
+// pointers carry no restrict qualifier and an empty asm with a memory clobber follows the
+// unit loads: otherwise the compiler, seeing loads of read-only memory, moves each unit's
+// loads down next to its stores and only one unit's loads are in flight at a time.
+template <typename T, int LAYOUT, bool ROTATE, typename PosFn, typename PlaceFn>
+__device__ __forceinline__ void rope_block(const T* src, T* dst, int nt, int Hkv, int D,
+                                           const double* __restrict__ inv_freq, PosFn pos_of,
+                                           PlaceFn place, double2* table, int32_t* err) {
 #pragma clang fp contract(off)
-  constexpr int HB = kRopeHeadGroup;
-  const int o0 = LAYOUT == 0 ? 8 * g : 16 * g;
-  const int o1 = LAYOUT == 0 ? D / 2 + 8 * g : 16 * g + 8;
-  Raw8<T> bu[2][HB], bw[2][HB];
-  auto load_group = [&](int buf, int h0) {
+  const int G = D / 16, per_tok = Hkv * G, units = nt * per_tok, half = D / 2;
+  const int64_t row = (int64_t)Hkv * D;
+  const int tid = threadIdx.x;
+  constexpr int NI = kRopeTablePairs / kRopeThreads;  // table entries per thread, at most
+  double f[NI];
+  int64_t kp[NI];
+  // the block's angles: entry q = tid + i * kRopeThreads is (token q / half, pair q % half)
+  auto angle_inputs = [&]() {
 #pragma unroll
-    for (int k = 0; k < HB; ++k)
-      if (h0 + k < Hkv) {
-        bu[buf][k] = ld8(src + (int64_t)(h0 + k) * D + o0);
-        bw[buf][k] = ld8(src + (int64_t)(h0 + k) * D + o1);
-      }
-  };
-  load_group(0, 0);
-  double c[8], s[8];
-  rope_angles(pos, inv_freq, g, c, s);
-  auto rotate_group = [&](int buf, int h0) {
-#pragma unroll
-    for (int k = 0; k < HB; ++k) {
-      if (h0 + k >= Hkv) break;
-      double u[8], w[8], a[8], b[8];
-      cvt8(bu[buf][k], u);
-      cvt8(bw[buf][k], w);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (LAYOUT == 0) {
-          a[j] = u[j];
-          b[j] = w[j];
-        } else {  // elements 16g .. 16g+15 hold pairs (2j, 2j+1)
-          a[j] = j < 4 ? u[2 * j] : w[2 * j - 8];
-          b[j] = j < 4 ? u[2 * j + 1] : w[2 * j - 7];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double ac = a[j] * c[j], bs = b[j] * s[j], as = a[j] * s[j], bc = b[j] * c[j];
-        const double ra = ac - bs, rb = as + bc;
-        if (LAYOUT == 0) {
-          u[j] = ra;
-          w[j] = rb;
-        } else if (j < 4) {
-          u[2 * j] = ra;
-          u[2 * j + 1] = rb;
-        } else {
-          w[2 * j - 8] = ra;
-          w[2 * j - 7] = rb;
-        }
-      }
-      T* dp = dst + (int64_t)(h0 + k) * D;
-      store8(dp + o0, u);
-      store8(dp + o1, w);
+    for (int i = 0; i < NI; ++i) {
+      const int q = min(tid + i * kRopeThreads, nt * half - 1);  // clamped: loads unconditional
+      const int t = q / half;
+      f[i] = inv_freq[q - t * half];
+      kp[i] = pos_of(t);
     }
   };
-  for (int h0 = 0; h0 < Hkv; h0 += 2 * HB) {
-    load_group(1, h0 + HB);
-    rotate_group(0, h0);
-    load_group(0, h0 + 2 * HB);
-    rotate_group(1, h0 + HB);
+  auto fill_table = [&]() {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = tid + i * kRopeThreads;
+      if (q >= nt * half) break;
+      double sn = 0.0, cs = 1.0;
+      if (place(kp[i], q / half).ok) sincos((double)kp[i] * f[i], &sn, &cs);
+      table[q] = make_double2(cs, sn);
+    }
+    __syncthreads();
+  };
+  if (ROTATE) {
+    angle_inputs();
+    if (SKV_ROPE_TRIG_FIRST) fill_table();
+  }
+  for (int base = 0; base < units; base += kRopeThreads * kRopeUnits) {
+    Raw8<T> ru[kRopeUnits], rw[kRopeUnits];
+    int ut[kRopeUnits], uh[kRopeUnits], ug[kRopeUnits];
+    int64_t up[kRopeUnits];
+#pragma unroll
+    for (int i = 0; i < kRopeUnits; ++i) {  // each unit's loads go out as soon as its address is known
+      const int u = min(base + tid + i * kRopeThreads, units - 1);  // clamped
+      ut[i] = u / per_tok;
+      const int r = u - ut[i] * per_tok;
+      uh[i] = r / G;
+      ug[i] = r - uh[i] * G;
+      up[i] = pos_of(ut[i]);
+      const T* sp = src + ut[i] * row + (int64_t)uh[i] * D;
+      ru[i] = ld8(sp + (LAYOUT == 0 ? 8 * ug[i] : 16 * ug[i]));
+      rw[i] = ld8(sp + (LAYOUT == 0 ? half + 8 * ug[i] : 16 * ug[i] + 8));
+    }
+    asm volatile("" ::: "memory");
+    if (ROTATE && !SKV_ROPE_TRIG_FIRST && base == 0) fill_table();
+#pragma unroll
+    for (int i = 0; i < kRopeUnits; ++i) {
+      if (base + tid + i * kRopeThreads >= units) break;
+      const RopeTok uk = place(up[i], ut[i]);
+      if (!uk.ok) {
+        if (ROTATE && uh[i] == 0 && ug[i] == 0) report(err, SKV_DEV_INDEX_RANGE);
+        continue;
+      }
+      T* dp = dst + uk.dst_row + (int64_t)uh[i] * D;
+      T* d0 = dp + (LAYOUT == 0 ? 8 * ug[i] : 16 * ug[i]);
+      T* d1 = dp + (LAYOUT == 0 ? half + 8 * ug[i] : 16 * ug[i] + 8);
+      if constexpr (!ROTATE) {
+        *(Raw8<T>*)d0 = ru[i];
+        *(Raw8<T>*)d1 = rw[i];
+      } else {
+        double x[8], y[8], a[8], b[8];
+        cvt8(ru[i], x);
+        cvt8(rw[i], y);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (LAYOUT == 0) {
+            a[j] = x[j];
+            b[j] = y[j];
+          } else {  // elements 16g .. 16g+15 hold pairs (2j, 2j+1)
+            a[j] = j < 4 ? x[2 * j] : y[2 * j - 8];
+            b[j] = j < 4 ? x[2 * j + 1] : y[2 * j - 7];
+          }
+        }
+        const double2* tp = table + ut[i] * half + 8 * ug[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double2 cs = tp[j];
+          const double ac = a[j] * cs.x, bs = b[j] * cs.y, as = a[j] * cs.y, bc = b[j] * cs.x;
+          const double ra = ac - bs, rb = as + bc;
+          if (LAYOUT == 0) {
+            x[j] = ra;
+            y[j] = rb;
+          } else if (j < 4) {
+            x[2 * j] = ra;
+            x[2 * j + 1] = rb;
+          } else {
+            y[2 * j - 8] = ra;
+            y[2 * j - 7] = rb;
+          }
+        }
+        store8(d0, x);
+        store8(d1, y);
+      }
+    }
   }
 }
 
-// The same 16 elements of every head, copied (V rows)
-template <typename T>
-__device__ __forceinline__ void copy_row(const T* src, T* dst, int Hkv, int D, int g) {
-  constexpr int V = 16 * sizeof(T) / 16;  // 16-byte vectors per 16 elements
-#pragma unroll 2
-  for (int h = 0; h < Hkv; ++h) {
-    const i32x4* sp = (const i32x4*)(src + (int64_t)h * D + 16 * g);
-    i32x4* dp = (i32x4*)(dst + (int64_t)h * D + 16 * g);
-    i32x4 r[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) r[v] = __builtin_nontemporal_load(sp + v);
-#pragma unroll
-    for (int v = 0; v < V; ++v) dp[v] = r[v];
-  }
+// Workgroup -> (batch element, token block, tensor): with V present the K and V workgroups
+// of a block alternate, so both kinds are in flight from the start (K workgroups begin with
+// their angle table, V workgroups with loads).
+struct RopeWg {
+  int b, t0, is_v;
+};
+__device__ __forceinline__ RopeWg rope_wg(int tb, int tblocks, bool has_v) {
+  const int nk = has_v ? 2 : 1, wg = blockIdx.x / nk;
+  const int b = wg / tblocks;
+  return RopeWg{b, (wg - b * tblocks) * tb, (int)blockIdx.x - wg * nk};
 }
 
 // Indexed slab write with rotated keys: cache[b, p] = rope(src[b, t], p), p = index[t]
-// (index == nullptr: start + t). Grid (B * tblocks, 1 + has V); thread -> (token t, group g).
-template <typename T, int LAYOUT>
+// (IDX false: start + t); rows with p outside [0, cap) are skipped and reported.
+// Grid B * tblocks * (1 + has V), tb tokens per workgroup.
+template <typename T, int LAYOUT, bool IDX>
 __global__ void __launch_bounds__(kRopeThreads)
-k_write_indexed_rope(const T* __restrict__ k_src, const T* __restrict__ v_src,
-                     T* __restrict__ k_cache, T* __restrict__ v_cache,
+k_write_indexed_rope(const T* k_src, const T* v_src, T* k_cache, T* v_cache,
                      const int64_t* __restrict__ index, int64_t start, int n, int cap, int Hkv,
-                     int D, const double* __restrict__ inv_freq, int tblocks, int32_t* err) {
-  const int gpt = D / 16, tpb = kRopeThreads / gpt;
-  const int b = blockIdx.x / tblocks, tb = blockIdx.x - b * tblocks;
-  const int t = tb * tpb + (int)threadIdx.x / gpt, g = (int)threadIdx.x % gpt;
-  if (t >= n) return;
-  const int64_t pos = index ? index[t] : start + t;
-  const bool is_v = blockIdx.y != 0;
-  if (pos < 0 || pos >= cap) {
-    if (!is_v && g == 0) report(err, SKV_DEV_INDEX_RANGE);
-    return;
-  }
+                     int D, const double* __restrict__ inv_freq, int tb, int tblocks, int32_t* err) {
+  extern __shared__ double2 table[];  // tb * D/2 entries
+  const RopeWg w = rope_wg(tb, tblocks, v_src != nullptr);
+  const int nt = min(tb, n - w.t0);
   const int64_t row = (int64_t)Hkv * D;
-  if (is_v) {
-    copy_row<T>(v_src + ((int64_t)b * n + t) * row, v_cache + ((int64_t)b * cap + pos) * row, Hkv, D, g);
-    return;
-  }
-  rope_row<T, LAYOUT>(k_src + ((int64_t)b * n + t) * row, k_cache + ((int64_t)b * cap + pos) * row,
-                      Hkv, D, g, pos, inv_freq);
+  auto pos_of = [&](int t) -> int64_t { return IDX ? index[w.t0 + t] : start + w.t0 + t; };
+  auto place = [&](int64_t p, int) {
+    const bool ok = p >= 0 && p < cap;
+    return RopeTok{p, ((int64_t)w.b * cap + (ok ? p : 0)) * row, ok};
+  };
+  const int64_t src_off = ((int64_t)w.b * n + w.t0) * row;
+  if (!w.is_v)
+    rope_block<T, LAYOUT, true>(k_src + src_off, k_cache, nt, Hkv, D, inv_freq, pos_of, place, table, err);
+  else
+    rope_block<T, LAYOUT, false>(v_src + src_off, v_cache, nt, Hkv, D, inv_freq, pos_of, place, table, err);
 }
 
 // Ring write with rotated keys: the chunk of batch element b goes to its reserved slot; row t
-// is rotated at position (counter[b] - 1) * C + t. Grid (B * tblocks, 1 + has V).
+// is rotated at position (counter[b] - 1) * C + t. Grid B * tblocks * (1 + has V).
 template <typename T, int LAYOUT>
 __global__ void __launch_bounds__(kRopeThreads)
-k_ring_write_rope(const T* __restrict__ k_src, const T* __restrict__ v_src,
-                  T* __restrict__ k_store, T* __restrict__ v_store, int32_t* meta, int B,
+k_ring_write_rope(const T* k_src, const T* v_src, T* k_store, T* v_store, int32_t* meta, int B,
                   const uint8_t* mask, int C, int n_slots, int Hkv, int D,
-                  const double* __restrict__ inv_freq, int tblocks, int32_t* err) {
+                  const double* __restrict__ inv_freq, int tb, int tblocks, int32_t* err) {
+  extern __shared__ double2 table[];  // tb * D/2 entries
   RingMeta m = ring_meta(meta, B);
-  if (blockIdx.x == 0 && blockIdx.y == 0) ring_commit(m, B, mask, C, n_slots, err);
-  const int gpt = D / 16, tpb = kRopeThreads / gpt;
-  const int b = blockIdx.x / tblocks, tb = blockIdx.x - b * tblocks;
-  const int t = tb * tpb + (int)threadIdx.x / gpt, g = (int)threadIdx.x % gpt;
-  if (t >= C || !selected(mask, b)) return;
-  const int slot = m.slot[b];
+  if (blockIdx.x == 0) ring_commit(m, B, mask, C, n_slots, err);
+  const RopeWg w = rope_wg(tb, tblocks, v_src != nullptr);
+  if (!selected(mask, w.b)) return;
+  const int slot = m.slot[w.b];
   if (slot < 0 || slot >= n_slots) return;  // unreserved (reported by workgroup 0) or corrupt
+  const int nt = min(tb, C - w.t0);
   const int64_t row = (int64_t)Hkv * D;
-  const int64_t src_off = ((int64_t)b * C + t) * row;
-  const int64_t dst_off = (((int64_t)b * n_slots + slot) * C + t) * row;
-  if (blockIdx.y != 0) {
-    copy_row<T>(v_src + src_off, v_store + dst_off, Hkv, D, g);
-    return;
-  }
-  rope_row<T, LAYOUT>(k_src + src_off, k_store + dst_off, Hkv, D, g,
-                      (int64_t)(m.counter[b] - 1) * C + t, inv_freq);
+  const int64_t pos0 = (int64_t)(m.counter[w.b] - 1) * C + w.t0;
+  const int64_t dst0 = (((int64_t)w.b * n_slots + slot) * C + w.t0) * row;
+  auto pos_of = [&](int t) -> int64_t { return pos0 + t; };
+  auto place = [&](int64_t p, int t) { return RopeTok{p, dst0 + t * row, true}; };
+  const int64_t src_off = ((int64_t)w.b * C + w.t0) * row;
+  if (!w.is_v)
+    rope_block<T, LAYOUT, true>(k_src + src_off, k_store, nt, Hkv, D, inv_freq, pos_of, place, table, err);
+  else
+    rope_block<T, LAYOUT, false>(v_src + src_off, v_store, nt, Hkv, D, inv_freq, pos_of, place, table, err);
 }
+
+// Tokens per workgroup: about kRopeThreads * kRopeUnits units, at most what the LDS table holds
+static int rope_tokens_per_block(int Hkv, int D) {
+  const int per_tok = Hkv * (D / 16);
+  int tb = (kRopeThreads * kRopeUnits) / per_tok;
+  if (tb < 1) tb = 1;
+  const int cap = kRopeTablePairs / (D / 2);
+  return tb < cap ? tb : cap;
+}
+
+static size_t rope_table_bytes(int tb, int D) { return (size_t)tb * (D / 2) * sizeof(double2); }
 
 template <typename T, int LAYOUT>
 static hipError_t write_indexed_rope_t(const void* k_src, const void* v_src, void* k_cache,
                                        void* v_cache, const int64_t* index, int64_t start, int B,
                                        int n, int cap, int Hkv, int D, const double* inv_freq,
                                        int32_t* err, hipStream_t s) {
-  const int tpb = kRopeThreads / (D / 16);
-  const int tblocks = (n + tpb - 1) / tpb;
-  dim3 grd((unsigned)((int64_t)B * tblocks), v_src ? 2 : 1);
-  hipLaunchKernelGGL((k_write_indexed_rope<T, LAYOUT>), grd, dim3(kRopeThreads), 0, s,
-                     (const T*)k_src, (const T*)v_src, (T*)k_cache, (T*)v_cache, index, start, n,
-                     cap, Hkv, D, inv_freq, tblocks, err);
+  const int tb = rope_tokens_per_block(Hkv, D);
+  const int tblocks = (n + tb - 1) / tb;
+  dim3 grd((unsigned)((int64_t)B * tblocks * (v_src ? 2 : 1)));
+  if (index)
+    hipLaunchKernelGGL((k_write_indexed_rope<T, LAYOUT, true>), grd, dim3(kRopeThreads),
+                       rope_table_bytes(tb, D), s, (const T*)k_src, (const T*)v_src, (T*)k_cache,
+                       (T*)v_cache, index, start, n, cap, Hkv, D, inv_freq, tb, tblocks, err);
+  else
+    hipLaunchKernelGGL((k_write_indexed_rope<T, LAYOUT, false>), grd, dim3(kRopeThreads),
+                       rope_table_bytes(tb, D), s, (const T*)k_src, (const T*)v_src, (T*)k_cache,
+                       (T*)v_cache, index, start, n, cap, Hkv, D, inv_freq, tb, tblocks, err);
   return hipGetLastError();
 }
 
@@ -242,12 +312,12 @@ static hipError_t ring_write_rope_t(const void* k_src, const void* v_src, void* 
                                     void* v_store, int32_t* meta, int B, const uint8_t* mask,
                                     int C, int n_slots, int Hkv, int D, const double* inv_freq,
                                     int32_t* err, hipStream_t s) {
-  const int tpb = kRopeThreads / (D / 16);
-  const int tblocks = (C + tpb - 1) / tpb;
-  dim3 grd((unsigned)((int64_t)B * tblocks), v_src ? 2 : 1);
-  hipLaunchKernelGGL((k_ring_write_rope<T, LAYOUT>), grd, dim3(kRopeThreads), 0, s,
+  const int tb = rope_tokens_per_block(Hkv, D);
+  const int tblocks = (C + tb - 1) / tb;
+  dim3 grd((unsigned)((int64_t)B * tblocks * (v_src ? 2 : 1)));
+  hipLaunchKernelGGL((k_ring_write_rope<T, LAYOUT>), grd, dim3(kRopeThreads), rope_table_bytes(tb, D), s,
                      (const T*)k_src, (const T*)v_src, (T*)k_store, (T*)v_store, meta, B, mask, C,
-                     n_slots, Hkv, D, inv_freq, tblocks, err);
+                     n_slots, Hkv, D, inv_freq, tb, tblocks, err);
   return hipGetLastError();
 }
 
