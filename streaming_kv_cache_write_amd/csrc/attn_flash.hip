@@ -503,10 +503,15 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
     __syncthreads();
     if (!*last_flag) return;
     // the sc1 loads see every store that completed before its piece was counted; the fence
-    // keeps the compiler from hoisting them above the count
+    // keeps the compiler from hoisting them above the count. Every partial, this piece's own
+    // included, is folded in piece order, so the result does not depend on which piece
+    // arrived last (folding into the empty start, m = -inf, copies the first partial exactly).
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    m = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
     for (int p = 0; p < fg.parts; ++p) {
-      if (p == part) continue;
       const auto r = rsrc(p);
       const float mp = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 4 * ml_off, 0, kFlashCoherent));
       const float lp =

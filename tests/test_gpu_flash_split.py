@@ -5,7 +5,8 @@ query heads, 37 query tiles: 74 items per XCD, the last 10 cut into pieces), and
 checked are those of the split items (batch element 1, queries from 3456 on) plus a few
 whole ones. Covered: host and device lengths, lengths so short that most pieces are empty,
 causal masking, packed K/V, the full-capacity arm, fp32 output with the LSE, fp16, D=64,
-and a workspace reused across calls (its arrival counters return to zero)."""
+a workspace reused across calls (its arrival counters return to zero), and bit-identical
+results across launches and graph replays whatever the pieces' arrival order."""
 import numpy as np
 import pytest
 import torch
@@ -153,3 +154,51 @@ def test_split_workspace_reused():
         check_attention(o[1, torch.from_numpy(split).to(DEV)], ref, dtype, f"reuse {lens}")
     torch.cuda.synchronize()
     assert not ws[:4 * 8 * 10].any()
+
+
+def test_split_is_deterministic_and_graph_replayable():
+    """The merge folds every piece's partial in piece order, whichever piece arrives last, so
+    repeated launches and replays of a captured graph give the same bits; the arrival counters
+    return to zero on every replay."""
+    dtype, D, cap = "bf16", 128, 8192
+    q, k, v = inputs(D, cap, dtype, 10)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    kl = torch.tensor([7000, 5000], dtype=torch.int32, device=DEV)
+    need = skv.attn_workspace_bytes(qd, kd, kv_len_dev=kl, max_seqlen_kv=cap)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(qd)
+
+    def call():
+        skv.attn_chunk_fwd(qd, kd, vd, out, kv_len_dev=kl, max_seqlen_kv=cap, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    first = out.clone()
+    for _ in range(4):
+        out.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), first.view(torch.int16))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(7.0)
+        call()  # eager work between replays
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), first.view(torch.int16)), rep
+        assert not ws[:4 * 8 * 10].any(), rep
+    whole, split = sample_rows(10)
+    ref, _ = oracle_rows(f64(q)[1], f64(k)[1], f64(v)[1], split, 5000, A.MASK_NONE)
+    check_attention(first[1, torch.from_numpy(split).to(DEV)], ref, dtype, "graph replay")
