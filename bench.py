@@ -305,16 +305,26 @@ def bench_ring(torch, skv, SI, dev):
                                                       max_seqlen_kv=rows)), dtype=torch.uint8, device=dev)
     no_ws = torch.zeros(16, dtype=torch.uint8, device=dev)  # too small: every item runs whole
 
-    def sequence():
+    def sequence(marks=None):
         ring.reset()
         for c in range(W.n_chunks):
+            if marks is not None:
+                marks[c].record()
             ring.reserve()
             for r in range(W.rewrites):
                 q, k, v = srcs[(c % 2) * 2 + (r % 2)]
                 ring.write(k, v)
                 skv.attn_chunk_fwd(q, ks, vs, out, kv_len_dev=ring.kv_len, max_seqlen_kv=rows, workspace=ws)
+        if marks is not None:
+            marks[W.n_chunks].record()
 
     seq_ms = time_gpu(torch, sequence, reps=3, warm=1)
+    # one more pass with an event at every chunk boundary: the step time of each chunk
+    # (reserve + rewrites x (write + attention)); chunk n_slots is the first to evict
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(W.n_chunks + 1)]
+    sequence(marks)
+    marks[-1].synchronize()
+    chunk_ms = [marks[c].elapsed_time(marks[c + 1]) for c in range(W.n_chunks)]
 
     def rolling_sequence():
         # the comparison arm: the same chunk lifecycle on a chronological buffer that moves its
@@ -386,6 +396,8 @@ def bench_ring(torch, skv, SI, dev):
         "workload": "ring: B=2, 12 heads, D=128, bf16, chunks of 4680, 7 slots (1 sink), 12 chunks x 4 rewrites",
         "sequence_ms": seq_ms, "sequence_tflops": flop_seq / seq_ms * 1e-9,
         "ms_per_rewrite_step": seq_ms / (W.n_chunks * W.rewrites),
+        "chunk_step_ms": [round(x, 4) for x in chunk_ms],
+        "first_eviction_chunk": W.n_slots,
         "saturated_attn_ms": attn_ms, "saturated_attn_tflops": flop_sat / attn_ms * 1e-9,
         "saturated_attn_frac_mfma": flop_sat / attn_ms * 1e-9 / MFMA_BF16_PEAK_TFS,
         "saturated_attn_tail_split_workspace_mb": ws.numel() / 1e6,
