@@ -8,8 +8,8 @@
 // loads -> math -> merge), so the kernel keeps that chain short and spreads the loads over
 // many CUs:
 //   * one workgroup of 4 wavefronts per (split, KV head g, batch element b); the split's key
-//     range is dealt out to the wavefronts in 16-key tiles, and each wavefront loads its next
-//     tile while it works on the current one;
+//     range is dealt out to the wavefronts in 16-key tiles, and each wavefront keeps the loads
+//     of its next two tiles in flight while it works on the current one;
 //   * the query rows of a GQA group (R = Tq * Hq/Hkv <= 16, padded to 16) share each K/V load.
 //     S^T = K Q^T runs on v_mfma_f32_16x16x32 with K straight from global memory as the A
 //     operand; its accumulator leaves, in each lane, four keys of one query row -- exactly the
@@ -104,6 +104,12 @@ __host__ __device__ __forceinline__ size_t dec_ml_floats(int B, int Hkv, int n_s
 // sc1 load from any CU, with no cache write-back or invalidate.
 constexpr int kDeviceCoherent = 16;  // buffer-op cache policy bits: sc1
 constexpr int kWaitVmcnt0 = 0x0F70;  // s_waitcnt vmcnt(0)
+// s_waitcnt vmcnt(2 * LT) (gfx9 encoding: vmcnt low bits 3:0, high bits 15:14; expcnt and
+// lgkmcnt at their maxima)
+template <int LT> constexpr int kWaitVmcntTwoTiles() {
+  static_assert(2 * LT < 64, "vmcnt field");
+  return (0x0F70 & ~0xC00F) | ((2 * LT) & 0xF) | (((2 * LT) >> 4) << 14);
+}
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const float* base, size_t floats) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(floats * sizeof(float)),
@@ -321,7 +327,7 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     split = blockIdx.x - bg * n_splits;
   }
   const int g = bg % a.Hkv, b = bg / a.Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n16 = lane & 15, G = lane >> 4;
   const int R = a.Tq * group;
   // workspace: arrival counters first (a fixed place for any split count), then partials
@@ -395,21 +401,29 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
 
   // Tile loads. K: lane (G, n16) takes key tile + n16, d = 32c + 8G .. +8 (the A operand of
   // S^T). V: lane takes key tile + lane/4, d = 8(4u + lane%4) .. +8 (whole rows per 4 lanes).
-  // Keys at or past `end` read as zero and issue no load.
+  // Every load is issued unconditionally -- keys at or past `end` read a row that exists
+  // (clamped) and are zeroed after the load -- so the outstanding loads form a fixed sequence
+  // and the waits before each tile's math cover only that tile.
+  constexpr int LT = DQ + VU;  // loads per tile
   auto load_tile = [&](int tile, uint4* kr, uint4* vr) {
-    const int jk = tile + n16;
+    const int jk = min(tile + n16, max(end - 1, 0));
     const T* kp = (FUSED && jk >= cur) ? knew : kbase;
 #pragma unroll
-    for (int c = 0; c < DQ; ++c)
-      kr[c] = jk < end ? *(const uint4*)(kp + (int64_t)jk * rstride + 32 * c + 8 * G)
-                       : make_uint4(0, 0, 0, 0);
-    const int jv = tile + (lane >> 2);
+    for (int c = 0; c < DQ; ++c) kr[c] = *(const uint4*)(kp + (int64_t)jk * rstride + 32 * c + 8 * G);
+    const int jv = min(tile + (lane >> 2), max(end - 1, 0));
     const T* vp = (FUSED && jv >= cur) ? vnew : vbase;
 #pragma unroll
-    for (int u = 0; u < VU; ++u)
-      vr[u] = jv < end ? *(const uint4*)(vp + (int64_t)jv * rstride + 8 * (4 * u + (lane & 3)))
-                       : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < VU; ++u) vr[u] = *(const uint4*)(vp + (int64_t)jv * rstride + 8 * (4 * u + (lane & 3)));
   };
+  // Keys at or past `end` count as zero rows. The mask is applied where the tile is used and
+  // passes through an empty asm: with a visible condition the compiler would turn the
+  // zeroing back into a load under that condition.
+  auto keep_mask = [&](int key) {
+    unsigned k = key < end ? ~0u : 0u;
+    asm volatile("" : "+v"(k));
+    return k;
+  };
+  auto masked = [](uint4 x, unsigned k) { return make_uint4(x.x & k, x.y & k, x.z & k, x.w & k); };
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 o[CB];
@@ -418,33 +432,30 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
   const float c2 = a.scale_log2;
   TP* vt = sm.v[wave];
 
-  uint4 kr[DQ], vr[VU];
-  const int t0 = start + kDecTile * wave;
-  load_tile(t0, kr, vr);
-  for (int tile = t0; tile < end; tile += kDecChunk) {
-    uint4 kn[DQ], vn[VU];
-    load_tile(tile + kDecChunk, kn, vn);  // next tile in flight during this one's math
-
+  // One tile's math: S^T, online softmax, P V.
+  auto process = [&](int tile, const uint4* kraw, const uint4* vraw) {
+    const unsigned kk = keep_mask(tile + n16), vk = keep_mask(tile + (lane >> 2));
     // V tile to LDS (row = key, converted to the P V type)
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       TP* dst = vt + (lane >> 2) * LDV + 8 * (4 * u + (lane & 3));
       if constexpr (PV16) {
-        const bf16_t* e = (const bf16_t*)&vr[u];
+        const uint4 vm = masked(vraw[u], vk);
+        const bf16_t* e = (const bf16_t*)&vm;
         typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 h8;
         h8 hv;
 #pragma unroll
         for (int k = 0; k < 8; ++k) hv[k] = (f16_t)(float)e[k];
         *(h8*)dst = hv;
       } else {
-        *(uint4*)dst = vr[u];
+        *(uint4*)dst = masked(vraw[u], vk);
       }
     }
 
     // S^T = K Q^T: s[j] = score(key tile + 4G + j, row n16)
     f32x4 s = f32x4{};
 #pragma unroll
-    for (int c = 0; c < DQ; ++c) s = MQ::qk(__builtin_bit_cast(vec8, kr[c]), qb[c], s);
+    for (int c = 0; c < DQ; ++c) s = MQ::qk(__builtin_bit_cast(vec8, masked(kraw[c], kk)), qb[c], s);
     float sv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = tile + 4 * G + j <= lim ? s[j] : -INFINITY;
@@ -484,14 +495,37 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
       const dec_s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dec_lds_s16x4*)vp);
       o[cb] = MP::pv(pa, __builtin_bit_cast(pvec4, x), o[cb]);
     }
-    // the V tile is rewritten by the next iteration of this wavefront
+    // the V tile is rewritten by this wavefront's next tile
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int c = 0; c < DQ; ++c) kr[c] = kn[c];
-#pragma unroll
-    for (int u = 0; u < VU; ++u) vr[u] = vn[u];
+  };
+
+  // This wavefront's tiles are t0, t0 + 64, ... below end (wave-uniform). Two tiles ahead:
+  // three register buffers in a loop unrolled by three, so no buffer is copied into another
+  // (a copy would wait for the newest loads), and the 0-2 remaining tiles after the loop.
+  // Before the loop one wait retires everything issued ahead of the first two tiles' loads
+  // (the queries, the new-row write), so the waits the compiler places in the loop count only
+  // tile loads.
+  const int t0 = start + kDecTile * wave;
+  const int n_tiles = end > t0 ? (end - t0 + kDecChunk - 1) / kDecChunk : 0;
+  if (n_tiles > 0) {  // then end >= 1 and every clamped row lies in the visited range
+    uint4 k0[DQ], v0[VU], k1[DQ], v1[VU], k2[DQ], v2[VU];
+    load_tile(t0, k0, v0);
+    load_tile(t0 + kDecChunk, k1, v1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntTwoTiles<LT>());
+    int i = 0;
+    for (; i + 3 <= n_tiles; i += 3) {
+      const int tile = t0 + i * kDecChunk;
+      load_tile(tile + 2 * kDecChunk, k2, v2);
+      process(tile, k0, v0);
+      load_tile(tile + 3 * kDecChunk, k0, v0);
+      process(tile + kDecChunk, k1, v1);
+      load_tile(tile + 4 * kDecChunk, k1, v1);
+      process(tile + 2 * kDecChunk, k2, v2);
+    }
+    if (i < n_tiles) process(t0 + i * kDecChunk, k0, v0);
+    if (i + 1 < n_tiles) process(t0 + (i + 1) * kDecChunk, k1, v1);
   }
 
   // row n16's sum: the four lane groups hold different keys of it
