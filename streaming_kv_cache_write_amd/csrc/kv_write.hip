@@ -132,10 +132,12 @@ k_ring_write(const i32x4* __restrict__ k_src, const i32x4* __restrict__ v_src,
     const int i = i0 + u * kCopyThreads;
     if (i < nv) r[u] = __builtin_nontemporal_load(src + i);
   }
+  // nontemporal stores: back-to-back chunk writes ran 7% faster with them (no change with a
+  // flushed cache before each write); the slab write measured slower cold with them
 #pragma unroll
   for (int u = 0; u < kCopyPer; ++u) {
     const int i = i0 + u * kCopyThreads;
-    if (i < nv) dst[i] = r[u];
+    if (i < nv) __builtin_nontemporal_store(r[u], dst + i);
   }
 }
 
