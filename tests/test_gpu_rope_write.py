@@ -154,3 +154,31 @@ def test_ring_rope_attention_equals_chronological_history():
     ref, _ = A.attend_prefix(f64(q[0]), kchron, vchron, len(kchron), A.MASK_NONE)
     check_attention(o[0], ref, dtype, "ring with rotated keys")
     ring.close()
+
+
+@pytest.mark.parametrize("shape", [
+    (16, 1, 1000),    # D=16, one head: 256 tokens per workgroup, the angle table exactly full
+    (512, 5, 37),     # 160 units per token, 6 tokens per workgroup
+    (1024, 17, 9),    # 1088 units per token: one token per workgroup, two passes of 1024 units
+    (64, 3, 1),       # a single token
+])
+@pytest.mark.parametrize("layout", [skv.ROPE_HALF, skv.ROPE_INTERLEAVED])
+def test_indexed_rope_write_block_shapes(shape, layout):
+    """Token blocks of every size the kernel plans: many tokens per workgroup with a full angle
+    table, a few, and one token whose units take two passes."""
+    D, Hkv, n = shape
+    dtype, B, cap = "bf16", 2, n + 50
+    k = SI.per_batch_normal(B, (n, Hkv, D), "misc", "k", chunk=70 + D, dtype=dtype)
+    v = SI.per_batch_normal(B, (n, Hkv, D), "misc", "v", chunk=70 + D, dtype=dtype)
+    kc = torch.zeros(B, cap, Hkv, D, dtype=TD[dtype], device=DEV)
+    vc = torch.zeros_like(kc)
+    rows = np.random.default_rng(D + n).permutation(cap)[:n].astype(np.int64)
+    f = inv_freq(D)
+    skv.kv_write_indexed_rope(kc, vc, k.to(DEV), v.to(DEV), torch.from_numpy(f).to(DEV),
+                              rope_layout=layout, index=torch.from_numpy(rows).to(DEV))
+    want_k, want_v = np.zeros((B, cap, Hkv, D)), np.zeros((B, cap, Hkv, D))
+    for b in range(B):
+        want_k[b, rows] = R.rope_keys(f64(k[b]), rows, f, layout, dtype)
+        want_v[b, rows] = f64(v[b])
+    assert_cache_equal(kc, want_k, dtype, f"K cache {shape}")
+    assert_cache_equal(vc, want_v, dtype, f"V cache {shape}")
