@@ -48,7 +48,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--only", default="", help="profiling aid: run only this part "
-                    "(decode | ring | multiuser | ragged | sweep | write)")
+                    "(decode | ring | multiuser | ragged | sweep | peaks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="counter-profiling aid: finish with one plain device copy of 256 MiB "
                     "(fresh buffers), whose FETCH_SIZE / WRITE_SIZE readings scale the "
@@ -547,6 +547,46 @@ def bench_sweep(torch, skv, SI, dev):
 
 
 # ----------------------------------------------------------------------------------------
+# measured ceilings: the library's MFMA-loop and copy probes, and a library GEMM
+# ----------------------------------------------------------------------------------------
+def bench_peaks(torch, skv, dev, rows):
+    res = {"what": "ceilings measured on this chip: skv_probe_mfma_bf16 (back-to-back 32x32x16 bf16 "
+                   "MFMAs from registers), skv_probe_copy (1 GiB copy, the cache writes' access pattern), "
+                   "and torch.matmul bf16 8192^3 (hipBLASLt) as a library reference"}
+    out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    flops = skv.probe_mfma_bf16(out, 2048, 2000)
+    ms = time_gpu(torch, lambda: skv.probe_mfma_bf16(out, 2048, 2000), reps=5)
+    res["mfma_bf16_tflops"] = flops / ms * 1e-9
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    byts = skv.probe_copy(dst, src)
+    ms = time_gpu(torch, lambda: skv.probe_copy(dst, src), reps=5)
+    res["copy_gbs"] = byts / ms * 1e-6
+    del src, dst
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    ms = time_gpu(torch, lambda: torch.matmul(a, b), reps=5)
+    res["gemm_bf16_tflops_library"] = 2 * 8192 ** 3 / ms * 1e-9
+    del a, b
+    mf, cp = res["mfma_bf16_tflops"], res["copy_gbs"]
+    frac = {}
+    ring, mu = rows.get("ring", {}), rows.get("multiuser", {})
+    if "saturated_attn_tflops" in ring:
+        frac["ring_saturated_attn_vs_mfma_probe"] = ring["saturated_attn_tflops"] / mf
+    if "chunk15_attn_tflops" in mu:
+        frac["chunk15_attn_vs_mfma_probe"] = mu["chunk15_attn_tflops"] / mf
+    if "slab_write_gbs" in mu:
+        frac["slab_write_vs_copy_probe"] = mu["slab_write_gbs"] / cp
+    if "ring_write_gbs" in ring:
+        frac["ring_write_vs_copy_probe"] = ring["ring_write_gbs"] / cp
+    sweep = rows.get("decode_sweep", {})
+    if "32768" in sweep:
+        frac["decode_32768_vs_copy_probe"] = sweep["32768"]["gbs_back_to_back"] / cp
+    res["fractions_of_measured"] = frac
+    return res
+
+
+# ----------------------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on a bounded sample of the decode job
 # ----------------------------------------------------------------------------------------
 def cpu_baseline(SI, dtype, n_steps=300):
@@ -617,7 +657,7 @@ def main():
 
     if args.only and args.only != "decode":
         fn = {"ring": bench_ring, "multiuser": bench_multiuser, "ragged": bench_ragged,
-              "sweep": bench_sweep}[args.only]
+              "sweep": bench_sweep, "peaks": lambda t, k, S, d: bench_peaks(t, k, d, {})}[args.only]
         print(json.dumps({args.only: fn(torch, skv, SI, dev)}))
         return
 
@@ -666,6 +706,11 @@ def main():
             except Exception as e:  # report, never hide
                 rows[name] = {"error": repr(e)}
             torch.cuda.empty_cache()
+        try:
+            line["measured_peaks"] = bench_peaks(torch, skv, dev, rows)
+        except Exception as e:  # report, never hide
+            line["measured_peaks"] = {"error": repr(e)}
+        torch.cuda.empty_cache()
         line["rows"] = rows
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(SI, args.dtype)

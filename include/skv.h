@@ -301,6 +301,22 @@ skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new,
                             void* v_cache, void* out, float* lse, int32_t* cursor_dev,
                             int32_t* kv_len_out_dev, const skv_attn_params* params, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Measurement probes (not part of the hot path): ceilings measured on the chip by kernels of
+ * this library, against which the hot-path kernels are also reported (the nominal peaks of
+ * the data sheet assume a 2.4 GHz clock the chip does not hold under matrix-core load).
+ *
+ * skv_probe_mfma_bf16: `workgroups` workgroups of 4 wavefronts, each wavefront issuing
+ *   4 * iters v_mfma_f32_32x32x16_bf16 from registers (32768 flops each, so
+ *   workgroups * 16 * iters * 32768 flops in all), then writing one float per lane to out_dev
+ *   [workgroups * 256] (caller device memory; the values are meaningless).
+ * skv_probe_copy: copies `bytes` (a multiple of 16) from src_dev to dst_dev (device, 16-byte
+ *   aligned, not overlapping) with the cache writes' access pattern; 2 * bytes of traffic.
+ * Errors: SKV_ERR_NULL, SKV_ERR_RANGE / SKV_ERR_SHAPE for sizes, SKV_ERR_ALIGN.
+ * ------------------------------------------------------------------------------------ */
+skv_status skv_probe_mfma_bf16(float* out_dev, int workgroups, int iters, void* stream);
+skv_status skv_probe_copy(void* dst_dev, const void* src_dev, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

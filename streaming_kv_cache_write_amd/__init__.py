@@ -11,4 +11,5 @@ from ._binding import (  # noqa: F401
     SKV_ERR_ALIGN, SKV_ERR_DTYPE, SKV_ERR_HIP, SKV_ERR_NULL, SKV_ERR_RANGE, SKV_ERR_SHAPE,
     SKV_ERR_UNSUPPORTED, SKV_F16, SKV_F32, SKV_OK, Ring, SkvError, attn_chunk_fwd, attn_decode_step,
     attn_workspace_bytes, kv_cursor_advance, kv_pack_ragged, kv_ragged_metadata, kv_roll_left,
-    kv_write_indexed, kv_write_indexed_rope, lib, make_params, skv_attn_params)
+    kv_write_indexed, kv_write_indexed_rope, lib, make_params, probe_copy, probe_mfma_bf16,
+    skv_attn_params)

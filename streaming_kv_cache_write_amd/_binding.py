@@ -80,6 +80,8 @@ _SIGS = {
     "attn_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, ctypes.POINTER(skv_attn_params), _vp]),
     "attn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               ctypes.POINTER(skv_attn_params), _vp]),
+    "skv_probe_mfma_bf16": (_i, [_vp, _i, _i, _vp]),
+    "skv_probe_copy": (_i, [_vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -418,3 +420,26 @@ def attn_decode_step(q, k_new, v_new, k_cache, v_cache, cursor, out=None, lse=No
                                 _ptr(out), _ptr(lse), _ptr(cursor), _ptr(kv_len_out), ctypes.byref(p),
                                 _stream(q.device)))
     return out
+
+
+# ------------------------------------------------------------------------------ measurement
+def probe_mfma_bf16(out, workgroups: int, iters: int) -> int:
+    """Launch the back-to-back bf16 MFMA probe; out: fp32 device tensor of workgroups*256.
+    Returns the flops it executes."""
+    _dev_tensor(out, "out", torch.float32)
+    if out.numel() < workgroups * 256:
+        raise ValueError("out needs workgroups * 256 floats")
+    _check(lib.skv_probe_mfma_bf16(_ptr(out), int(workgroups), int(iters), _stream(out.device)))
+    return int(workgroups) * 16 * int(iters) * 32768
+
+
+def probe_copy(dst, src) -> int:
+    """Copy src to dst (device tensors of equal byte size) with the probe copy kernel.
+    Returns the bytes of traffic (read + write)."""
+    _dev_tensor(dst, "dst")
+    _dev_tensor(src, "src")
+    nb = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nb:
+        raise ValueError("dst and src differ in size")
+    _check(lib.skv_probe_copy(_ptr(dst), _ptr(src), nb, _stream(src.device)))
+    return 2 * nb

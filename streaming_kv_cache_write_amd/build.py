@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libskv.so")
-SOURCES = ["api.hip", "kv_write.hip", "kv_rope.hip", "attn_f32.hip", "attn_flash.hip", "attn_decode.hip"]
+SOURCES = ["api.hip", "kv_write.hip", "kv_rope.hip", "attn_f32.hip", "attn_flash.hip", "attn_decode.hip",
+           "peaks.hip"]
 ARCH = os.environ.get("SKV_OFFLOAD_ARCH", "gfx950")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic (the kernels use

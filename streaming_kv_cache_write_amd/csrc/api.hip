@@ -28,6 +28,8 @@ hipError_t launch_ring_write_rope(const void*, const void*, void*, void*, int32_
                                   const uint8_t*, int, int, int, int, int, const double*, int,
                                   int32_t*, hipStream_t);
 hipError_t launch_attn_f32(const AttnArgs&, int, hipStream_t);
+hipError_t launch_peak_mfma_bf16(float*, int, int, hipStream_t);
+hipError_t launch_peak_copy(void*, const void*, size_t, hipStream_t);
 hipError_t launch_attn_flash(const AttnArgs&, int, int, int, int, void*, size_t, hipStream_t);
 size_t flash_workspace_bytes(int B, int Hq, int Tq, int D, int key_bound);
 hipError_t launch_attn_decode(const AttnArgs&, int, int, int, void*, int, hipStream_t);
@@ -462,6 +464,26 @@ skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new,
   return hip_status(launch_attn_decode(a, p->dtype, p->out_dtype, p->D, p->workspace, splits,
                                        (hipStream_t)stream),
                     "attn_decode_step launch");
+}
+
+// ---------------------------------------------------------------------------------------
+// Measurement probes
+// ---------------------------------------------------------------------------------------
+skv_status skv_probe_mfma_bf16(float* out_dev, int workgroups, int iters, void* stream) {
+  if (!out_dev) return fail(SKV_ERR_NULL, "out_dev is NULL");
+  if (workgroups < 1 || iters < 1) return fail(SKV_ERR_RANGE, "need workgroups >= 1 and iters >= 1");
+  if ((uintptr_t)out_dev & 3) return fail(SKV_ERR_ALIGN, "out_dev must be 4-byte aligned");
+  return hip_status(launch_peak_mfma_bf16(out_dev, workgroups, iters, (hipStream_t)stream),
+                    "skv_probe_mfma_bf16 launch");
+}
+
+skv_status skv_probe_copy(void* dst_dev, const void* src_dev, size_t bytes, void* stream) {
+  if (!dst_dev || !src_dev) return fail(SKV_ERR_NULL, "dst_dev and src_dev must be non-NULL");
+  if (bytes % 16) return fail(SKV_ERR_SHAPE, "bytes must be a multiple of 16 (got %zu)", bytes);
+  if (!aligned16(dst_dev) || !aligned16(src_dev)) return fail(SKV_ERR_ALIGN, "buffers must be 16-byte aligned");
+  if (bytes / 16 / 512 >= 0x7fffffffu) return fail(SKV_ERR_SHAPE, "copy too large");
+  if (bytes == 0) return ok();
+  return hip_status(launch_peak_copy(dst_dev, src_dev, bytes, (hipStream_t)stream), "skv_probe_copy launch");
 }
 
 }  // extern "C"

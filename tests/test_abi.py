@@ -246,3 +246,15 @@ def test_rope_write_host_errors():
     g = lib.kv_ring_write_rope
     # ring, k_src, v_src, inv_freq, layout, mask, err, stream
     assert g(None, P, None, P, 0, None, None, None) == skv.SKV_ERR_NULL
+
+
+def test_probe_host_errors():
+    f, c = lib.skv_probe_mfma_bf16, lib.skv_probe_copy
+    assert f(None, 1, 1, None) == skv.SKV_ERR_NULL
+    assert f(P, 0, 1, None) == skv.SKV_ERR_RANGE
+    assert f(P, 1, 0, None) == skv.SKV_ERR_RANGE
+    assert f(P + 2, 1, 1, None) == skv.SKV_ERR_ALIGN
+    assert c(None, P, 16, None) == skv.SKV_ERR_NULL
+    assert c(P, P, 24, None) == skv.SKV_ERR_SHAPE
+    assert c(BAD, P, 16, None) == skv.SKV_ERR_ALIGN
+    assert c(P, P, 0, None) == skv.SKV_OK  # nothing to do, nothing launched
