@@ -621,6 +621,52 @@ def cpu_baseline(SI, dtype, n_steps=300):
                       f"fp64 numpy oracle incl. its slab writes (capacity 32768)"}
 
 
+def cpu_baseline_rows(SI):
+    """The fp64 oracle on bounded samples of the other workloads (a few seconds in all):
+    attention over a sample of query rows of one (b, h) at the workload's key count, and one
+    cache write of the workload's size. Rates are per sample and so per query row."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import cache as Cc
+    rng = np.random.default_rng(0)
+
+    def attn_rate(n_q, L, D, mask=A.MASK_NONE, Tq=None):
+        Tq = Tq or n_q
+        q = rng.standard_normal((n_q, 1, D))
+        k = rng.standard_normal((L, 1, D))
+        v = rng.standard_normal((L, 1, D))
+        t0 = time.perf_counter()
+        allowed = np.stack([A.visible_keys(Tq - n_q + i, Tq, L, mask) for i in range(n_q)])
+        A.attend_keys(q, k, v, allowed)
+        secs = time.perf_counter() - t0
+        flop = 4 * D * int(allowed.sum())
+        return {"tflops": flop / secs * 1e-12, "seconds": round(secs, 3),
+                "sample": f"{n_q} query rows x {L} keys, one head"}
+
+    def write_rate(rows, H, D, fn):
+        src = rng.standard_normal((1, rows, H, D))
+        t0 = time.perf_counter()
+        fn(src)
+        secs = time.perf_counter() - t0
+        return {"gbs": 2 * src.size * ELEM / secs * 1e-9, "seconds": round(secs, 3),
+                "sample": f"{rows} rows x {H} heads x {D}, bytes counted at 2 B per element"}
+
+    R, M, G = SI.Ring(), SI.MultiUser(), SI.Ragged()
+    attn_rate(64, 4096, 128)  # warm-up: BLAS threads
+    res = {"what": "fp64 numpy oracle on samples of the other workloads, host cores as in cpu_baseline"}
+    res["ring_saturated_attention"] = attn_rate(256, R.n_slots * R.C, R.D)
+    res["multiuser_chunk15_attention"] = attn_rate(256, M.cap, M.D, A.MASK_BLOCK_CAUSAL, Tq=M.chunk)
+    for L0, L1 in G.skews:
+        res[f"ragged_{L0}_{L1}_attention"] = attn_rate(8192, L1, G.D)
+    ring = Cc.RingPhysical(R.n_slots, R.sink, R.C, (R.H, R.D))
+    ring.reserve()
+    res["ring_write"] = write_rate(R.C, R.H, R.D, lambda s: ring.write(s[0]))
+    slab = np.zeros((1, M.cap, M.H, M.D))
+    res["slab_write"] = write_rate(M.chunk, M.H, M.D,
+                                   lambda s: Cc.slab_write_indexed(slab, s, np.arange(M.chunk)))
+    return res
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("attn_decode.hip", "common.h"):
@@ -715,6 +761,8 @@ def main():
         line["rows"] = rows
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(SI, args.dtype)
+        if not args.no_rows:
+            line["cpu_baseline_rows"] = cpu_baseline_rows(SI)
     if args.copy_calibration:
         line["copy_calibration_bytes"] = copy_calibration(torch, dev)
     print(json.dumps(line))
