@@ -241,10 +241,13 @@ skv_status kv_pack_ragged(void* k_packed, void* v_packed, const void* k_padded, 
  *     merged in the same launch. Without one (NULL or smaller) every item runs whole; the
  *     results agree up to the order of the final sums;
  *   - fp32 needs none.
- * The workspace must be zero-filled once before its first use: its first bytes hold arrival
- * counters (int32, at offset 0) that every call leaves at zero again, so one zero-filled
- * workspace of the largest size needed can serve every later call. Calls sharing one
- * workspace must not overlap in time (they are ordered when issued on one stream).
+ * The workspace must be zero-filled once before its first use: its first 64 KiB hold arrival
+ * counters (int32) that every call leaves at zero again, and every kind of call keeps its
+ * partial results after those 64 KiB, so one zero-filled workspace of the largest size needed
+ * can serve any later sequence of calls. Calls sharing one workspace must not overlap in time
+ * (they are ordered when issued on one stream). Decode-sized chunks take the split-K path only
+ * while B*Hkv < 16384 (one counter per batch element and KV head); larger batches of them
+ * run the chunk path (attn_decode_step returns SKV_ERR_UNSUPPORTED).
  * max_seqlen_kv: optional host bound on any batch element's key count; it only sizes the
  * split grids and the workspace when the lengths live on the device (0 = use cap / the host
  * kv_len).

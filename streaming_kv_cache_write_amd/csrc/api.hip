@@ -80,9 +80,13 @@ constexpr int kDecodeMaxRows = 16;
 // Path taken by attn_chunk_fwd for a validated parameter set.
 enum Path { PATH_F32, PATH_FLASH, PATH_DECODE };
 
+// (the split-K path counts arrivals per (b, KV head) in the workspace's shared counter area,
+// so it takes B*Hkv below its size; larger batches of short chunks run the flash path)
 Path choose_path(const skv_attn_params& p) {
   if (p.dtype == SKV_F32) return PATH_F32;
-  if (p.Tq <= kDecodeMaxTq && p.Tq * (p.Hq / p.Hkv) <= kDecodeMaxRows) return PATH_DECODE;
+  if (p.Tq <= kDecodeMaxTq && p.Tq * (p.Hq / p.Hkv) <= kDecodeMaxRows &&
+      (int64_t)p.B * p.Hkv < kWsCounterInts)
+    return PATH_DECODE;
   return PATH_FLASH;
 }
 
@@ -428,8 +432,8 @@ skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new,
   if (st != SKV_OK) return st;
   if (p->Tq == 0) return ok();
   if (choose_path(v) != PATH_DECODE)
-    return fail(SKV_ERR_UNSUPPORTED, "the fused decode step needs bf16/f16, Tq <= %d and "
-                "Tq*Hq/Hkv <= %d", kDecodeMaxTq, kDecodeMaxRows);
+    return fail(SKV_ERR_UNSUPPORTED, "the fused decode step needs bf16/f16, Tq <= %d, "
+                "Tq*Hq/Hkv <= %d and B*Hkv < %d", kDecodeMaxTq, kDecodeMaxRows, kWsCounterInts);
   if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)cursor_dev & 3) ||
       ((uintptr_t)kv_len_out_dev & 3) || (lse && ((uintptr_t)lse & 3)))
     return fail(SKV_ERR_ALIGN, "misaligned k_new / v_new / cursor / kv_len_out / lse");

@@ -88,9 +88,8 @@ constexpr int kDecRows = 16;    // query rows per KV head (MFMA block; R <= 16 a
 constexpr int kDecMaxSplits = 32;
 constexpr float kDecRescaleLog2 = 8.f;
 
-__host__ __device__ __forceinline__ size_t dec_counter_floats(int B, int Hkv) {
-  return (((size_t)B * Hkv + 1 + 63) / 64) * 64;  // B*Hkv split counters + 1, 256-byte multiple
-}
+// the shared counter area: B*Hkv split counters + 1 (host-checked to fit)
+__host__ __device__ __forceinline__ size_t dec_counter_floats(int, int) { return kWsCounterInts; }
 __host__ __device__ __forceinline__ size_t dec_o_floats(int B, int Hkv, int D, int n_splits) {
   return (size_t)B * Hkv * n_splits * kDecRows * D;
 }

@@ -125,11 +125,11 @@ struct FlashGrid {
   float* ws;  // parts > 1: arrival counters, then the pieces' partials
 };
 
-// Workspace of the tail split: int32 arrival counters (one per split item, left at zero by
-// every launch), padded to 256 bytes, then per (split item, piece) a block of 256 lanes x
-// (D/2 floats of O^T + the reference max + the row sum), lane-interleaved.
+// Workspace of the tail split: the shared counter area (one int32 arrival counter per split
+// item, at most 8 x 63, left at zero by every launch), then per (split item, piece) a block of
+// 256 lanes x (D/2 floats of O^T + the reference max + the row sum), lane-interleaved.
 __host__ __device__ constexpr int flash_piece_floats(int D) { return 256 * (D / 2 + 2); }
-__host__ __device__ constexpr int flash_counter_floats(int n_split) { return (n_split + 63) & ~63; }
+__host__ __device__ constexpr int flash_counter_floats(int) { return kWsCounterInts; }
 
 // Device-coherent (sc1) buffer accesses, as agent-scope atomic stores and loads take: the
 // pieces of one item run on one XCD, but nothing ties a later launch reusing the workspace to

@@ -35,6 +35,12 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
 template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (f16_t)x; }
 
+// Attention workspace: its first kWsCounterInts int32 are arrival counters, which every launch
+// leaves at zero; partials follow. The counter area has the same size for every kernel that
+// takes a workspace, so one workspace of the largest size needed can serve any sequence of
+// calls: no call's counters ever overlap another call's partials.
+constexpr int kWsCounterInts = 16384;  // 64 KiB
+
 // Which keys batch element b attends to, read from the device metadata at run time.
 //   prefix mode: rows [0, len) of the batch element's cap-row slab; with the full-capacity
 //                arm all cap rows are visited and rows >= len are masked.

@@ -138,15 +138,29 @@ def flash_tail_plan(B, Hq, Tq, key_bound):
 ])
 def test_flash_tail_split_workspace(B, Hq, Tq, kv_len, D):
     """attn_workspace_bytes of chunk-sized calls: zero unless the tail split is planned, then
-    the arrival counters (padded to 256 bytes) and one partial of 256 lanes x (D/2 + 2)
-    floats per piece."""
+    the shared 64 KiB counter area and one partial of 256 lanes x (D/2 + 2) floats per piece."""
     k, R = flash_tail_plan(B, Hq, Tq, kv_len)
     n_split = 8 * R
-    want = 0 if k == 1 else 4 * (((n_split + 63) // 64) * 64 + n_split * k * 256 * (D // 2 + 2))
+    want = 0 if k == 1 else 4 * (16384 + n_split * k * 256 * (D // 2 + 2))  # 64 KiB of counters first
     p = params(B=B, Hq=Hq, Hkv=Hq if Hq % 2 else Hq // 2, Tq=Tq, D=D, cap=kv_len, kv_len=kv_len)
     assert lib.attn_workspace_bytes(ctypes.byref(p)) == want
     if (B, Hq, Tq) == (2, 12, 4680):
         assert (k, R) == (4, 47)
+
+
+def test_decode_workspace_layout_and_batch_limit():
+    """Decode-sized calls: 64 KiB of counters, then o partials [B*Hkv*splits*16*D] and (m, l)
+    [B*Hkv*splits*32] fp32; with B*Hkv >= 16384 they take the chunk path (no split-K
+    workspace) and the fused step refuses them."""
+    p = params(Tq=1, kv_len=4096, cap=4096, B=1, Hq=32, Hkv=8)
+    splits = 32  # min(ceil(4096 / 128), 256 / 8)
+    want = 4 * (16384 + 8 * splits * 16 * 128 + 8 * splits * 32)
+    assert lib.attn_workspace_bytes(ctypes.byref(p)) == want
+    big = params(Tq=1, kv_len=64, cap=64, B=2048, Hq=64, Hkv=8)  # B*Hkv = 16384
+    assert lib.attn_workspace_bytes(ctypes.byref(big)) == 0
+    f = lib.attn_decode_step
+    # q, k_new, v_new, k_cache, v_cache, out, lse, cursor, kv_len_out, params, stream
+    assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(big), None) == skv.SKV_ERR_UNSUPPORTED
 
 
 def test_write_host_errors():

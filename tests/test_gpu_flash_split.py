@@ -202,3 +202,33 @@ def test_split_is_deterministic_and_graph_replayable():
     whole, split = sample_rows(10)
     ref, _ = oracle_rows(f64(q)[1], f64(k)[1], f64(v)[1], split, 5000, A.MASK_NONE)
     check_attention(first[1, torch.from_numpy(split).to(DEV)], ref, dtype, "graph replay")
+
+
+def test_workspace_shared_with_decode_calls():
+    """One workspace of the largest size serves tail-split chunk calls and split-K decode
+    calls in any order: every kind of call keeps its counters in the same 64 KiB area and
+    leaves them at zero, and its partials after it. Each result equals the same call on a
+    fresh zero-filled workspace, bit for bit."""
+    q, k, v = inputs(128, 8192, "bf16", 11)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    kl = torch.tensor([6000, 7000], dtype=torch.int32, device=DEV)
+    fkw = dict(kv_len_dev=kl, max_seqlen_kv=8192)
+    # decode: 16 batch elements x 8 KV heads, 32 query heads, 3000 keys
+    Bd, Hqd, Hkvd, Ld = 16, 32, 8, 3000
+    qdec = torch.randn(Bd, 1, Hqd, 128, device=DEV).to(torch.bfloat16)
+    kdec = torch.randn(Bd, Ld, Hkvd, 128, device=DEV).to(torch.bfloat16)
+    vdec = torch.randn(Bd, Ld, Hkvd, 128, device=DEV).to(torch.bfloat16)
+    need_f = skv.attn_workspace_bytes(qd, kd, **fkw)
+    need_d = skv.attn_workspace_bytes(qdec, kdec, kv_len=Ld)
+    assert need_f > 0 and need_d > 0
+    fresh = lambda n: torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ref_f = skv.attn_chunk_fwd(qd, kd, vd, workspace=fresh(need_f), **fkw)
+    ref_d = skv.attn_chunk_fwd(qdec, kdec, vdec, kv_len=Ld, workspace=fresh(need_d))
+    ws = fresh(max(need_f, need_d))
+    for rep in range(2):
+        o_f = skv.attn_chunk_fwd(qd, kd, vd, workspace=ws, **fkw)
+        o_d = skv.attn_chunk_fwd(qdec, kdec, vdec, kv_len=Ld, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o_f.view(torch.int16), ref_f.view(torch.int16)), rep
+        assert torch.equal(o_d.view(torch.int16), ref_d.view(torch.int16)), rep
+        assert not ws[:65536].any(), rep
