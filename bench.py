@@ -18,7 +18,7 @@ Printed as one JSON line:
   rows          the other hot-path workloads measured in the same run (ring, multi-user slab,
                 ragged cross-attention, decode kv_len sweep with cold caches, slab writes).
 
-`python bench.py --gpus N` with N > 1 exits: this build runs on one GPU.
+`python bench.py --gpus N` with N > 1 exits: the library runs on one GPU.
 """
 from __future__ import annotations
 
@@ -693,7 +693,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "this build has no multi-GPU path.", file=sys.stderr)
+              "the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
 

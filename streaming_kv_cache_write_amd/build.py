@@ -1,7 +1,7 @@
 """Compile libskv.so (the HIP kernels and the C ABI of include/skv.h) for gfx950, in tree.
 
 Usage: python streaming_kv_cache_write_amd/build.py   (a script: importing the package would
-load the library this builds).
+load the library that this script compiles).
 Every call recompiles; objects go to _build/ beside this file, the library to libskv.so.
 """
 from __future__ import annotations
