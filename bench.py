@@ -705,7 +705,10 @@ def main():
     if args.only and args.only != "decode":
         fn = {"ring": bench_ring, "multiuser": bench_multiuser, "ragged": bench_ragged,
               "sweep": bench_sweep, "peaks": lambda t, k, S, d: bench_peaks(t, k, d, {})}[args.only]
-        print(json.dumps({args.only: fn(torch, skv, SI, dev)}))
+        res = {args.only: fn(torch, skv, SI, dev)}
+        if args.copy_calibration:
+            res["copy_calibration_bytes"] = copy_calibration(torch, dev)
+        print(json.dumps(res))
         return
 
     d = bench_decode(torch, skv, SI, dev, args)
