@@ -549,10 +549,12 @@ def bench_sweep(torch, skv, SI, dev):
 # ----------------------------------------------------------------------------------------
 # measured ceilings: the library's MFMA-loop and copy probes, and a library GEMM
 # ----------------------------------------------------------------------------------------
-def bench_peaks(torch, skv, dev, rows):
+def bench_peaks(torch, skv, SI, dev, rows):
     res = {"what": "ceilings measured on this chip: skv_probe_mfma_bf16 (back-to-back 32x32x16 bf16 "
-                   "MFMAs from registers), skv_probe_copy (1 GiB copy, the cache writes' access pattern), "
-                   "and a bf16 GEMM 8192 x 8192 x 16384 through torch (hipBLASLt) as a library reference"}
+                   "MFMAs from registers), skv_probe_copy (1 GiB copy, the cache writes' access pattern; "
+                   "also, cold, at the ring and slab writes' own sizes, since a copy's rate depends on "
+                   "its size), and a bf16 GEMM 8192 x 8192 x 16384 through torch (hipBLASLt) as a "
+                   "library reference"}
     out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
     flops = skv.probe_mfma_bf16(out, 2048, 2000)
     ms = time_gpu(torch, lambda: skv.probe_mfma_bf16(out, 2048, 2000), reps=5)
@@ -563,6 +565,19 @@ def bench_peaks(torch, skv, dev, rows):
     ms = time_gpu(torch, lambda: skv.probe_copy(dst, src), reps=5)
     res["copy_gbs"] = byts / ms * 1e-6
     del src, dst
+    # the same copy at the sizes of one ring rewrite and one slab chunk write (K and V together,
+    # read + written), each after a cache flush like the writes' own cold timings
+    flush = make_flush(torch, dev)
+    R, M = SI.Ring(), SI.MultiUser()
+    same = {"ring_write": 2 * R.B * R.C * R.H * R.D * ELEM, "slab_write": 2 * M.B * M.chunk * M.H * M.D * ELEM}
+    res["copy_gbs_cold_same_size"] = {}
+    for name, each_way in same.items():
+        src = torch.empty(each_way, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        byts = skv.probe_copy(dst, src)
+        ms = time_gpu(torch, lambda: skv.probe_copy(dst, src), reps=10, flush=flush)
+        res["copy_gbs_cold_same_size"][name] = {"bytes": byts, "us": ms * 1e3, "gbs": byts / ms * 1e-6}
+        del src, dst
     # x @ w^T with w [N, K] row-major (the fastest of the layouts and shapes tried here)
     a = torch.randn(8192, 16384, dtype=torch.bfloat16, device=dev)
     w = torch.randn(8192, 16384, dtype=torch.bfloat16, device=dev)
@@ -576,10 +591,13 @@ def bench_peaks(torch, skv, dev, rows):
         frac["ring_saturated_attn_vs_mfma_probe"] = ring["saturated_attn_tflops"] / mf
     if "chunk15_attn_tflops" in mu:
         frac["chunk15_attn_vs_mfma_probe"] = mu["chunk15_attn_tflops"] / mf
+    same = res["copy_gbs_cold_same_size"]
     if "slab_write_gbs" in mu:
         frac["slab_write_vs_copy_probe"] = mu["slab_write_gbs"] / cp
+        frac["slab_write_vs_copy_same_size"] = mu["slab_write_gbs"] / same["slab_write"]["gbs"]
     if "ring_write_gbs" in ring:
         frac["ring_write_vs_copy_probe"] = ring["ring_write_gbs"] / cp
+        frac["ring_write_vs_copy_same_size"] = ring["ring_write_gbs"] / same["ring_write"]["gbs"]
     sweep = rows.get("decode_sweep", {})
     if "32768" in sweep:
         frac["decode_32768_vs_copy_probe"] = sweep["32768"]["gbs_back_to_back"] / cp
@@ -704,7 +722,7 @@ def main():
 
     if args.only and args.only != "decode":
         fn = {"ring": bench_ring, "multiuser": bench_multiuser, "ragged": bench_ragged,
-              "sweep": bench_sweep, "peaks": lambda t, k, S, d: bench_peaks(t, k, d, {})}[args.only]
+              "sweep": bench_sweep, "peaks": lambda t, k, S, d: bench_peaks(t, k, S, d, {})}[args.only]
         res = {args.only: fn(torch, skv, SI, dev)}
         if args.copy_calibration:
             res["copy_calibration_bytes"] = copy_calibration(torch, dev)
@@ -757,7 +775,7 @@ def main():
                 rows[name] = {"error": repr(e)}
             torch.cuda.empty_cache()
         try:
-            line["measured_peaks"] = bench_peaks(torch, skv, dev, rows)
+            line["measured_peaks"] = bench_peaks(torch, skv, SI, dev, rows)
         except Exception as e:  # report, never hide
             line["measured_peaks"] = {"error": repr(e)}
         torch.cuda.empty_cache()
