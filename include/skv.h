@@ -230,7 +230,8 @@ skv_status kv_pack_ragged(void* k_packed, void* v_packed, const void* k_padded, 
  *   p/mask_block, integer division; mask_block = 1 is CAUSAL).
  * GQA: query head h reads KV head h / (Hq/Hkv); heads are never expanded [FS, Problem].
  * q, out: [B, Tq, Hq, D]; lse (optional, fp32 [B, Hq, Tq]) = natural-log sum of
- * exp(scale*score). scale == 0 means 1/sqrt(D). D in {64, 128}.
+ * exp(scale*score). scale == 0 means 1/sqrt(D). D in {64, 128}; B*Tq*Hq < 2^31 and
+ * Hq*D <= 2^21 (else SKV_ERR_SHAPE).
  * dtype: SKV_F32 (exact fp32 arithmetic), SKV_BF16 or SKV_F16 (matrix-core products with
  * fp32 accumulation and fp32 softmax). out_dtype: dtype or SKV_F32.
  * Workspace (caller device memory, 16-byte aligned, attn_workspace_bytes(params) bytes):

@@ -133,6 +133,9 @@ skv_status validate_attn(const void* q, const void* k, const void* v, const void
     return fail(SKV_ERR_ALIGN, "q, k, v and out must be 16-byte aligned");
   const int64_t elems = (int64_t)p->B * p->Tq * p->Hq;
   if (elems > 0x7fffffff) return fail(SKV_ERR_SHAPE, "B*Tq*Hq too large");
+  // the kernels address a 64-row block of q, k, v or out rows with 32-bit byte offsets
+  if ((int64_t)p->Hq * p->D > (1 << 21))
+    return fail(SKV_ERR_SHAPE, "Hq*D=%lld too large (at most 2^21)", (long long)p->Hq * p->D);
   return SKV_OK;
 }
 

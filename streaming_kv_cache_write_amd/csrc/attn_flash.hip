@@ -538,19 +538,47 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
 
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (q_ok) {
+  // The output goes out as whole rows. In the accumulator layout a lane holds 4 columns of
+  // one query row, so a direct store instruction would touch 32 rows with 16 bytes each; each
+  // wavefront instead writes its 32 x D block into one idle tile buffer (16-byte granules
+  // XOR-swizzled by row) and reads it back as 16-byte granules, 4 whole rows per instruction.
+  // Only this wavefront touches its buffer, and LDS operations of a wavefront complete in
+  // order, so no barrier is needed between the two passes.
+  constexpr int OB = D * (int)sizeof(OutT);  // bytes per output row
+  constexpr int GR = OB / 16;                // 16-byte granules per row
+  static_assert(32 * OB <= TILE, "a wavefront's output block must fit one tile buffer");
+  if (split_id >= 0) __syncthreads();  // the merging workgroup: every wave has read last_flag
+  unsigned char* const stage = wave == 0 ? Ks0 : wave == 1 ? Ks1 : wave == 2 ? Vs0 : Vs1;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = 32 * db + 8 * i + 4 * hi;
-        store4<OutT>(out_row + d0, o[db][4 * i] * inv, o[db][4 * i + 1] * inv,
-                     o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
-      }
-    if (a.lse && hi == 0) {
-      const float mm = m == -INFINITY ? 0.f : m;
-      a.lse[((int64_t)b * a.Hq + h) * a.Tq + my_q] = mm * a.scale + logf(ltot);
+    for (int i = 0; i < 4; ++i) {
+      const int byte = (32 * db + 8 * i + 4 * hi) * (int)sizeof(OutT);
+      const int pos = (((byte >> 4) ^ (l32 % GR)) << 4) | (byte & 15);
+      store4<OutT>((OutT*)(stage + l32 * OB + pos), o[db][4 * i] * inv, o[db][4 * i + 1] * inv,
+                   o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
     }
+  // rows past Tq fall outside the store resource's range and are dropped
+  const int q0 = qt * kFlashBM + wave * 32;  // first query row of this wavefront
+  const int row_stride = a.Hq * OB;           // host-checked: 32 rows of it fit an int
+  const int n_rows = max(min(32, a.Tq - q0), 0);
+  const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+      (unsigned char*)a.out + (((int64_t)b * a.Tq + q0) * a.Hq + h) * OB, (short)0,
+      n_rows > 0 ? (n_rows - 1) * row_stride + OB : 0, kBufferRsrcWord3);
+  u32x4 val[GR / 2];
+#pragma unroll
+  for (int k = 0; k < GR / 2; ++k) {
+    const int f = k * 64 + lane, row = f / GR, gr = f % GR;
+    val[k] = *(const u32x4*)(stage + row * OB + ((gr ^ (row % GR)) << 4));
+  }
+#pragma unroll
+  for (int k = 0; k < GR / 2; ++k) {
+    const int f = k * 64 + lane, row = f / GR, gr = f % GR;
+    __builtin_amdgcn_raw_buffer_store_b128(val[k], rout, row * row_stride + gr * 16, 0, 0);
+  }
+  if (q_ok && a.lse && hi == 0) {
+    const float mm = m == -INFINITY ? 0.f : m;
+    a.lse[((int64_t)b * a.Hq + h) * a.Tq + my_q] = mm * a.scale + logf(ltot);
   }
 }
 

@@ -69,6 +69,7 @@ def attn(p, q=P, k=P, v=P, out=P):
 @pytest.mark.parametrize("kw,ptrs,status", [
     ({}, dict(q=None), skv.SKV_ERR_NULL),
     (dict(Hq=6, Hkv=4), {}, skv.SKV_ERR_SHAPE),
+    (dict(Hq=16400, Hkv=2), {}, skv.SKV_ERR_SHAPE),  # Hq*D past 2^21 (32-bit row-block offsets)
     (dict(D=96), {}, skv.SKV_ERR_UNSUPPORTED),
     (dict(dtype=7), {}, skv.SKV_ERR_DTYPE),
     (dict(out_dtype=skv.SKV_F16), {}, skv.SKV_ERR_DTYPE),
