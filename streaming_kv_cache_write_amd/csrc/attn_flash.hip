@@ -203,17 +203,20 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
   const bool q_ok = my_q < a.Tq;
   OutT* out_row = (OutT*)a.out + (((int64_t)b * a.Tq + my_q) * a.Hq + h) * D;
 
-  // this wave's queries as the B operand of S^T = K Q^T (loaded once; they need no key
+  // this wave's queries, the B operand of S^T = K Q^T, loaded once. They need no key
   // metadata, so they go out first and their latency overlaps the metadata read and the
-  // first K/V loads -- one wait, after the prologue, covers them all)
-  vec qreg[DC];
-  {
-    const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + my_q) * a.Hq + h) * D + 8 * hi;
+  // first K/V loads. The loads read whole rows (RPI rows of 16-byte granules per
+  // instruction, instead of 32 rows x 32 bytes in the operand layout); the prologue
+  // rearranges them through LDS.
+  constexpr int RPI = 64 / GPR;  // query rows per load instruction
+  const int q0 = qt * kFlashBM + wave * 32;  // first query row of this wavefront
+  vec qraw[DC], qreg[DC];
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      if (q_ok) qreg[c] = *(const vec*)(qp + 16 * c);
-      else qreg[c] = vec{};
-    }
+  for (int c = 0; c < DC; ++c) {
+    const int row = c * RPI + lane / GPR;
+    const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + q0 + row) * a.Hq + h) * D + 8 * (lane % GPR);
+    if (q0 + row < a.Tq) qraw[c] = *(const vec*)qp;
+    else qraw[c] = vec{};
   }
 
   const KeySet ks = key_set(a, b);
@@ -446,13 +449,36 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
     dma(kbase, 0, Ks[0], koff);
     dma(vbase, 0, Vs[0], voff);
     if (n_tiles > 1) dma(kbase, BN, Ks[1], koff);
+  }
+  // Q into the operand layout (lane (l32, hi) of register c: granule 2c + hi of row l32)
+  // through this wave's quarter of Vs1, idle until the first step: 16 rows per pass, granules
+  // XOR-swizzled by row. One wavefront per region and LDS operations of a wavefront complete
+  // in order, so the passes need no barrier.
+  {
+    unsigned char* const qs = Vs1 + wave * (TILE / 4);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int c = pass * DC / 2; c < (pass + 1) * DC / 2; ++c) {
+        const int lr = c * RPI + lane / GPR - 16 * pass, gr = lane % GPR;
+        *(vec*)(qs + lr * ROWB + 16 * (gr ^ (lr % GPR))) = qraw[c];
+      }
+      const int lr = l32 - 16 * pass;
+      if (lr >= 0 && lr < 16) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+          qreg[c] = *(const vec*)(qs + lr * ROWB + 16 * ((2 * c + hi) ^ (lr % GPR)));
+      }
+    }
+  }
+  if (n_tiles > 0) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     convert_v(Vs[0]);
     __syncthreads();
     qk(0, sacc[0]);
     __syncthreads();  // every wave has read Ks[0] before tile 0's step refills it
   }
-  // Q's loads are complete on every path from here (the prologue waited for them), so the
+  // Q's loads are complete on every path from here (their values went to LDS), so the
   // compiler counts nothing outstanding at the head of the tile loop, where a wait would
   // also cover the next tiles' loads
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -559,7 +585,6 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
                    o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
     }
   // rows past Tq fall outside the store resource's range and are dropped
-  const int q0 = qt * kFlashBM + wave * 32;  // first query row of this wavefront
   const int row_stride = a.Hq * OB;           // host-checked: 32 rows of it fit an int
   const int n_rows = max(min(32, a.Tq - q0), 0);
   const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
