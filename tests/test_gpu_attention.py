@@ -236,3 +236,24 @@ def test_decode_steps_through_the_device_cursor(dtype):
         o_ref, _ = A.attend_prefix(f64(rng_q[0, T + i:T + i + 1]), kref[0], vref[0], T + i + 1)
         check_attention(o[0], o_ref, dtype, f"step {i}")
     assert int(kv_len) == T + steps
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("out_dtype", [None, torch.float32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_output_rows_stay_inside_out(dtype, out_dtype, D):
+    """Outputs leave as whole rows, 32 per wavefront: with Tq = 37 the second wavefront of a
+    query tile has 5 rows and the last two none. Every output row matches the oracle and the
+    NaN canaries on both sides of `out` (one extra query row of every head) stay untouched."""
+    B, Tq, Hq, Hkv, cap, kv_len = 2, 37, 3, 1, 200, 170
+    q, k, v = make(B, Tq, Hq, Hkv, D, cap, dtype, seed=D + 11)
+    ot = out_dtype or TD[dtype]
+    pad = Hq * D  # one query row of all heads
+    n = B * Tq * Hq * D
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=ot, device=DEV)
+    out = buf[pad:pad + n].view(B, Tq, Hq, D)
+    skv.attn_chunk_fwd(q.to(DEV), k.to(DEV), v.to(DEV), out, kv_len=kv_len, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, _ = oracle_prefix(q, k, v, [kv_len] * B)
+    check_attention(out, o_ref, dtype, f"D={D} out={ot}")
+    assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[pad + n:]).all(), "write outside out"
