@@ -34,6 +34,10 @@
 //   * Workgroup ids are remapped so the query tiles of one (b, h) run on the same XCD and
 //     share its L2 copy of K/V (dispatch hands consecutive workgroup ids to the 8 XCDs in turn),
 //     with the (b, h) pairs dealt round-robin over the XCDs so unequal heads stay balanced.
+//   * Q and O cross global memory as whole rows: Q is loaded 16 bytes per lane in row order
+//     and moved into the operand layout through LDS in the prologue; each wavefront's
+//     normalised output block is staged in an idle tile buffer and stored 4 rows per
+//     instruction (the operand and accumulator layouts would touch 32 rows per instruction).
 //   * Tail split (optional, needs a workspace): when the last round of workgroups would leave
 //     many of the CU slots idle, the items of that round are cut by key range into a few
 //     pieces. Each piece stores its unnormalised O^T, reference max and row sums; the last
