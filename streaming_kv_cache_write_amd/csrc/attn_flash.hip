@@ -212,15 +212,23 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
   // first K/V loads. The loads read whole rows (RPI rows of 16-byte granules per
   // instruction, instead of 32 rows x 32 bytes in the operand layout); the prologue
   // rearranges them through LDS.
+  // Rows past Tq lie outside the load resource's range and read as zeros, so every load is
+  // unconditional (per-row branches made the compiler wait for the first load to land).
   constexpr int RPI = 64 / GPR;  // query rows per load instruction
   const int q0 = qt * kFlashBM + wave * 32;  // first query row of this wavefront
+  const int row_stride = a.Hq * D * (int)sizeof(T);  // host-checked: 32 rows fit an int
+  const int n_qrows = max(min(32, a.Tq - q0), 0);
   vec qraw[DC], qreg[DC];
+  {
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const T*)a.q + (((int64_t)b * a.Tq + q0) * a.Hq + h) * D), (short)0,
+        n_qrows > 0 ? (n_qrows - 1) * row_stride + D * (int)sizeof(T) : 0, kBufferRsrcWord3);
 #pragma unroll
-  for (int c = 0; c < DC; ++c) {
-    const int row = c * RPI + lane / GPR;
-    const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + q0 + row) * a.Hq + h) * D + 8 * (lane % GPR);
-    if (q0 + row < a.Tq) qraw[c] = *(const vec*)qp;
-    else qraw[c] = vec{};
+    for (int c = 0; c < DC; ++c) {
+      const int row = c * RPI + lane / GPR;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, row * row_stride + 16 * (lane % GPR), 0, 0);
+      __builtin_memcpy(&qraw[c], &x, 16);
+    }
   }
 
   const KeySet ks = key_set(a, b);
@@ -589,11 +597,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
                    o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
     }
   // rows past Tq fall outside the store resource's range and are dropped
-  const int row_stride = a.Hq * OB;           // host-checked: 32 rows of it fit an int
-  const int n_rows = max(min(32, a.Tq - q0), 0);
+  const int out_stride = a.Hq * OB;           // host-checked: 32 rows of it fit an int
   const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
       (unsigned char*)a.out + (((int64_t)b * a.Tq + q0) * a.Hq + h) * OB, (short)0,
-      n_rows > 0 ? (n_rows - 1) * row_stride + OB : 0, kBufferRsrcWord3);
+      n_qrows > 0 ? (n_qrows - 1) * out_stride + OB : 0, kBufferRsrcWord3);
   u32x4 val[GR / 2];
 #pragma unroll
   for (int k = 0; k < GR / 2; ++k) {
@@ -603,7 +610,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
 #pragma unroll
   for (int k = 0; k < GR / 2; ++k) {
     const int f = k * 64 + lane, row = f / GR, gr = f % GR;
-    __builtin_amdgcn_raw_buffer_store_b128(val[k], rout, row * row_stride + gr * 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(val[k], rout, row * out_stride + gr * 16, 0, 0);
   }
   if (q_ok && a.lse && hi == 0) {
     const float mm = m == -INFINITY ? 0.f : m;
