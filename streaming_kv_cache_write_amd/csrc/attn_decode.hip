@@ -349,6 +349,28 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     }
   }
 
+  // fused step: wave 0 of split 0 copies this head's slice of the new rows into the cache.
+  // The sources do not depend on the cursor, so their loads go out here, before the cursor
+  // read; the stores follow once this wave's first tile loads are issued, so neither waits
+  // for the copy. Lane (t, c8): row t, 16-byte granule c8 (Tq * D/8 <= 64 on this path).
+  constexpr int VPR = D / 8;
+  const int64_t rstride = (int64_t)a.Hkv * D;
+  const bool copier = FUSED && split == 0 && wave == 0;  // wave-uniform
+  const int cp_t = min(lane / VPR, a.Tq - 1), cp_c8 = lane % VPR;
+  uint4 cpk, cpv;  // set and used only by the copier wave
+  if (copier) {
+    const int64_t src = ((int64_t)b * a.Tq + cp_t) * rstride + (int64_t)g * D + 8 * cp_c8;
+    cpk = *(const uint4*)((const T*)a.k_new + src);
+    cpv = *(const uint4*)((const T*)a.v_new + src);
+  }
+  auto copy_new_rows = [&](int cur_, const KeySet& ks_) {
+    if (copier && ks_.ok && lane < a.Tq * VPR) {
+      const int64_t dst = (ks_.base_row + cur_ + cp_t) * rstride + (int64_t)g * D + 8 * cp_c8;
+      *(uint4*)((T*)a.k + dst) = cpk;
+      *(uint4*)((T*)a.v + dst) = cpv;
+    }
+  };
+
   // a rejected batch element still takes part in the arrival count, with empty splits
   int cur = 0;  // fused step: the write position of this step
   KeySet ks;
@@ -376,7 +398,6 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     lim = rl < lim ? rl : lim;
   }
 
-  const int64_t rstride = (int64_t)a.Hkv * D;
   const T* kbase = (const T*)a.k + ks.base_row * rstride + (int64_t)g * D;
   const T* vbase = (const T*)a.v + ks.base_row * rstride + (int64_t)g * D;
   // fused step: key j >= cur is new row j - cur of k_new/v_new (rows of batch element b)
@@ -385,17 +406,6 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
   if constexpr (FUSED) {
     knew = (const T*)a.k_new + (int64_t)b * a.Tq * rstride + (int64_t)g * D - (int64_t)cur * rstride;
     vnew = (const T*)a.v_new + (int64_t)b * a.Tq * rstride + (int64_t)g * D - (int64_t)cur * rstride;
-    if (split == 0 && wave == 0 && ks.ok) {  // this head's slice of the new rows goes into the cache
-      constexpr int VPR = D / 8;
-      for (int i = lane; i < a.Tq * VPR; i += 64) {
-        const int t = i / VPR, c8 = i - t * VPR;
-        const int64_t row = cur + t;
-        *(uint4*)((T*)a.k + ks.base_row * rstride + row * rstride + (int64_t)g * D + 8 * c8) =
-            *(const uint4*)(knew + row * rstride + 8 * c8);
-        *(uint4*)((T*)a.v + ks.base_row * rstride + row * rstride + (int64_t)g * D + 8 * c8) =
-            *(const uint4*)(vnew + row * rstride + 8 * c8);
-      }
-    }
   }
 
   // Tile loads. K: lane (G, n16) takes key tile + n16, d = 32c + 8G .. +8 (the A operand of
@@ -513,6 +523,7 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     load_tile(t0, k0, v0);
     load_tile(t0 + kDecChunk, k1, v1);
     __builtin_amdgcn_s_waitcnt(kWaitVmcntTwoTiles<LT>());
+    if constexpr (FUSED) copy_new_rows(cur, ks);
     int i = 0;
     for (; i + 3 <= n_tiles; i += 3) {
       const int tile = t0 + i * kDecChunk;
@@ -525,6 +536,8 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     }
     if (i < n_tiles) process(t0 + i * kDecChunk, k0, v0);
     if (i + 1 < n_tiles) process(t0 + (i + 1) * kDecChunk, k1, v1);
+  } else if constexpr (FUSED) {
+    copy_new_rows(cur, ks);  // (the copier wave always has tiles when the step is valid)
   }
 
   // row n16's sum: the four lane groups hold different keys of it
