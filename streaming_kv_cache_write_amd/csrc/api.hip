@@ -32,7 +32,7 @@ hipError_t launch_peak_mfma_bf16(float*, int, int, hipStream_t);
 hipError_t launch_peak_copy(void*, const void*, size_t, hipStream_t);
 hipError_t launch_attn_flash(const AttnArgs&, int, int, int, int, void*, size_t, hipStream_t);
 size_t flash_workspace_bytes(int B, int Hq, int Tq, int D, int key_bound);
-hipError_t launch_attn_decode(const AttnArgs&, int, int, int, void*, int, hipStream_t);
+hipError_t launch_attn_decode(const AttnArgs&, int, int, int, void*, int, int, hipStream_t);
 int decode_splits(int B, int Hkv, int max_len);
 size_t decode_workspace_bytes(int B, int Hkv, int D, int n_splits);
 }  // namespace skv
@@ -365,7 +365,12 @@ skv_status kv_pack_ragged(void* k_packed, void* v_packed, const void* k_padded, 
 }
 
 size_t attn_workspace_bytes(const skv_attn_params* p) {
-  if (!p || validate_attn((void*)16, (void*)16, (void*)16, (void*)16, p) != SKV_OK) return 0;
+  if (!p) {
+    fail(SKV_ERR_NULL, "params is NULL");
+    return (size_t)-1;
+  }
+  if (validate_attn((void*)16, (void*)16, (void*)16, (void*)16, p) != SKV_OK) return (size_t)-1;
+  ok();
   if (choose_path(*p) == PATH_F32) return 0;
   if (choose_path(*p) == PATH_FLASH) return flash_workspace_bytes(p->B, p->Hq, p->Tq, p->D, key_bound(*p));
   const int splits = decode_splits(p->B, p->Hkv, key_bound(*p));
@@ -413,7 +418,8 @@ skv_status attn_chunk_fwd(const void* q, const void* k, const void* v, void* out
       if (p->workspace_bytes < need)
         return fail(SKV_ERR_RANGE, "workspace of %zu bytes < %zu required", p->workspace_bytes, need);
       if (!aligned16(p->workspace)) return fail(SKV_ERR_ALIGN, "workspace must be 16-byte aligned");
-      return hip_status(launch_attn_decode(a, p->dtype, p->out_dtype, p->D, p->workspace, splits, s),
+      return hip_status(launch_attn_decode(a, p->dtype, p->out_dtype, p->D, p->workspace, splits,
+                                           key_bound(*p), s),
                         "attn_chunk_fwd (decode) launch");
     }
   }
@@ -441,8 +447,8 @@ skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new,
       ((uintptr_t)kv_len_out_dev & 3) || (lse && ((uintptr_t)lse & 3)))
     return fail(SKV_ERR_ALIGN, "misaligned k_new / v_new / cursor / kv_len_out / lse");
   v.kv_len_dev = nullptr;
-  const int splits = decode_splits(p->B, p->Hkv, p->max_seqlen_kv > 0 && p->max_seqlen_kv < p->cap
-                                                     ? p->max_seqlen_kv : p->cap);
+  const int bound = p->max_seqlen_kv > 0 && p->max_seqlen_kv < p->cap ? p->max_seqlen_kv : p->cap;
+  const int splits = decode_splits(p->B, p->Hkv, bound);
   const size_t need = decode_workspace_bytes(p->B, p->Hkv, p->D, splits);
   if (!p->workspace) return fail(SKV_ERR_NULL, "the decode step needs a workspace of %zu bytes", need);
   if (p->workspace_bytes < need)
@@ -469,7 +475,7 @@ skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new,
   a.cursor = cursor_dev;
   a.kv_len_out = kv_len_out_dev;
   return hip_status(launch_attn_decode(a, p->dtype, p->out_dtype, p->D, p->workspace, splits,
-                                       (hipStream_t)stream),
+                                       bound, (hipStream_t)stream),
                     "attn_decode_step launch");
 }
 

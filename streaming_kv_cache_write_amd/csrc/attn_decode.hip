@@ -80,11 +80,13 @@ template <> struct DecMma<f16_t> {
   }
 };
 
-constexpr int kDecWaves = 4;    // wavefronts per workgroup
 constexpr int kDecTile = 16;    // keys per wavefront tile (one MFMA block of keys)
-constexpr int kDecChunk = kDecWaves * kDecTile;  // keys per workgroup round; splits are whole chunks
-constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecRows = 16;    // query rows per KV head (MFMA block; R <= 16 are used)
+// Workgroup shape: W wavefronts take W tiles (a chunk of 16 W keys) per round.
+template <int W> struct DecShape {
+  static constexpr int waves = W, chunk = kDecTile * W, threads = 64 * W;
+};
+constexpr int kDecWaves = 4;
 constexpr int kDecMaxSplits = 32;
 constexpr float kDecRescaleLog2 = 8.f;
 
@@ -146,19 +148,37 @@ __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// Exchanges with lane ^ 16 and lane ^ 32 by permlane swaps (VALU, no LDS round trip): with
+// both operands x, the swap returns the two rows (or halves) of each pair, in either order.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
 __device__ __forceinline__ float max32(float x) {  // over each 32-lane half of the wavefront
   x = fmaxf(x, dpp_f<kDppXor1>(x));
   x = fmaxf(x, dpp_f<kDppXor2>(x));
   x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
   x = fmaxf(x, dpp_f<kDppMirror>(x));
-  return fmaxf(x, __shfl_xor(x, 16, 64));
+  return max_xor16(x);
 }
 __device__ __forceinline__ float sum32(float x) {
   x += dpp_f<kDppXor1>(x);
   x += dpp_f<kDppXor2>(x);
   x += dpp_f<kDppHalfMirror>(x);
   x += dpp_f<kDppMirror>(x);
-  return x + __shfl_xor(x, 16, 64);
+  return sum_xor16(x);
 }
 
 __device__ __forceinline__ float f4_get(float4 v, int j) {
@@ -189,51 +209,53 @@ __device__ __forceinline__ void write_lse(const AttnArgs& a, int group, int b, i
   a.lse[((int64_t)b * a.Hq + h) * a.Tq + t] = L > 0.f ? M * a.scale + logf(L) : -INFINITY;
 }
 
-// The last workgroup of (b, g): merge the n_splits partials. Every load is unconditional
+// The last workgroup of (b, g): merge the n_active partials. Every load is unconditional
 // (indices clamped, invalid entries neutralised afterwards), so no load waits on a branch. The
 // (m, l) loads go first, then the first batch of o loads; step 1 -- thread (row r, split s),
 // 32 splits per half-wavefront -- reduces over the splits to the weight exp2((m_s - M) c2) / L
 // of each partial (L = the weighted sum of the l_s), kept in LDS, while the o loads are in
 // flight. Step 2: thread (row quad, column, split residue mod tpp) sums its splits' weighted
 // o; the tpp threads of a pair are adjacent lanes and add by DPP.
-template <int D, typename OutT>
-__device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, int RQ,
-                                             __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml,
-                                             float (*wt)[kDecRows], int b, int g, int n_splits) {
+template <int D, typename OutT, int NT>
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, int RQ, const float* o_bg,
+                                             __amdgpu_buffer_rsrc_t rml, float (*wt)[kDecRows], int b,
+                                             int g, int n_active, int n_splits) {
+  const __amdgpu_buffer_rsrc_t ro_bg = ws_rsrc(o_bg, (size_t)n_active * 4 * D * 4);
   constexpr int kMB = 16;  // o loads in flight per thread
   const int R = a.Tq * group, rows = 4 * RQ;
   const float c2 = a.scale_log2;
-  constexpr int NQ = (kDecRows * 32 + kDecThreads - 1) / kDecThreads;  // (row, split) rounds
+  constexpr int NQ = (kDecRows * 32 + NT - 1) / NT;  // (row, split) rounds
   const int pairs = RQ * D;  // (row quad, column)
-  const int tpp = 4 * pairs <= kDecThreads ? 4 : 2 * pairs <= kDecThreads ? 2 : 1;
+  const int tpp = 4 * pairs <= NT ? 4 : 2 * pairs <= NT ? 2 : 1;
   const int t = threadIdx.x, sub = t & (tpp - 1), p0 = t / tpp;
-  const int p_step = kDecThreads / tpp;
-  const int last_split = n_splits - 1;
+  const int p_step = NT / tpp;
+  const int last_split = n_active - 1;
 
-  float mm[NQ], ll[NQ];  // (m, l) of (row q / 32, split q % 32) for q = t + kDecThreads k
+  float mm[NQ], ll[NQ];  // (m, l) of (row q / 32, split q % 32) for q = t + NT k
 #pragma unroll
   for (int k = 0; k < NQ; ++k) {
-    const int q = t + kDecThreads * k;
+    const int q = t + NT * k;
     const size_t base = dec_ml_base(b, g, min(q & 31, last_split), a.Hkv, n_splits);
     const int r = min(q >> 5, rows - 1);
     mm[k] = load_coherent1(rml, base + r);
     ll[k] = load_coherent1(rml, base + kDecRows + r);
   }
+  // o partials of this (b, g) through a resource that ends after the active splits: a load of a
+  // split past them returns zeros and moves no data
   float4 ob[kMB];
   auto load_batch = [&](int p, int s0) {
     const int pc = min(p, pairs - 1);
     const int rq = pc / D, col = pc - rq * D;
 #pragma unroll
     for (int i = 0; i < kMB; ++i)
-      ob[i] = load_coherent4(
-          ro, (dec_o_quad(b, g, min(s0 + i * tpp, last_split), rq, a.Hkv, n_splits, D) + col) * 4);
+      ob[i] = load_coherent4(ro_bg, ((size_t)((s0 + i * tpp) * 4 + rq) * D + col) * 4);
   };
   load_batch(p0, sub);
 
 #pragma unroll
   for (int k = 0; k < NQ; ++k) {
-    const int q = t + kDecThreads * k, r = q >> 5, sp = q & 31;
-    const bool ok = r < rows && sp < n_splits;
+    const int q = t + NT * k, r = q >> 5, sp = q & 31;
+    const bool ok = r < rows && sp < n_active;
     // a clamped split index repeats the row's last split, which leaves the max unchanged;
     // it gets weight 0 (its l, a finite partial of this launch, then adds nothing)
     const float M = max32(mm[k]);
@@ -249,14 +271,14 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, int R
     const int pc = min(p, pairs - 1);
     const int rq = pc / D, col = pc - rq * D;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = sub; s0 < n_splits; s0 += kMB * tpp) {
+    for (int s0 = sub; s0 < n_active; s0 += kMB * tpp) {
       if (p != p0 || s0 != sub) load_batch(p, s0);
       float4 w4[kMB];
 #pragma unroll
       for (int i = 0; i < kMB; ++i) w4[i] = *(const float4*)&wt[min(s0 + i * tpp, last_split)][4 * rq];
 #pragma unroll
       for (int i = 0; i < kMB; ++i) {
-        const bool ok = s0 + i * tpp < n_splits;
+        const bool ok = s0 + i * tpp < n_active;
         acc = make_float4(fmaf(ok ? w4[i].x : 0.f, ob[i].x, acc.x), fmaf(ok ? w4[i].y : 0.f, ob[i].y, acc.y),
                           fmaf(ok ? w4[i].z : 0.f, ob[i].z, acc.z), fmaf(ok ? w4[i].w : 0.f, ob[i].w, acc.w));
       }
@@ -277,17 +299,28 @@ __device__ __forceinline__ void merge_splits(const AttnArgs& a, int group, int R
   }
 }
 
-// Workgroup = kDecWaves wavefronts per (split, KV head g, batch element b). The split covers
-// whole 64-key chunks of the visited range; wavefront w takes the 16-key tiles at offsets
-// 16w, 16w + 64, ... of it.
+// Workgroup = W wavefronts per (split, KV head g, batch element b). The split covers whole
+// chunks (16 W keys) of the visited range; wavefront w takes the 16-key tiles at offsets 16w,
+// 16w + 16W, ... of it. Splits past the last one holding keys leave at once: they store no
+// partial and are not waited for, so the merge reads only the splits that did work.
 // FUSED: one launch per decode step with the write cursor on the device (attn_decode_step):
 // c = *cursor; the new rows k_new/v_new [B, Tq, Hkv, D] are written to cache rows c .. c+Tq-1
 // and attended over as keys c .. c+Tq-1 straight from the sources (no wavefront of this launch
-// reads a cache row another one writes); the last (b, g) to finish sets *cursor = c+Tq and
-// kv_len_out[:] = c+Tq, after every wavefront has read the cursor.
-template <typename T, int D, typename OutT, bool FUSED>
-__global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int group, float* ws,
-                                                                int n_splits) {
+// reads a cache row another one writes). Every workgroup counts itself in once it has read the
+// cursor; the last one to do so sets *cursor = c+Tq and kv_len_out[:] = c+Tq.
+// SPEC: the first tiles of every wavefront are known before the length is read -- each split
+// holds at most one chunk at the host's key bound (then that chunk is the split's only one), or
+// there is one split per head (then the first two tiles sit at 16w and 16w + 16W) -- so their
+// loads go out with the queries, in the shadow of the cursor / kv_len read (prefix mode only;
+// FUSED only with Tq = 1, where the one new key is taken from k_new/v_new registers loaded
+// alongside, where each tile is used). If the device length exceeds the bound so that a split
+// holds more than one chunk, the early loads are dropped and the split is loaded again.
+template <typename T, int D, typename OutT, bool FUSED, bool SPEC, int W>
+__global__ void __launch_bounds__(DecShape<W>::threads) k_attn_decode(AttnArgs a, int group, float* ws,
+                                                                        int n_splits) {
+  constexpr int CH = DecShape<W>::chunk;
+  constexpr int NT = DecShape<W>::threads;
+  constexpr bool PATCH = FUSED && SPEC;
   // P V in fp16 (V converted while staged) for bf16 inputs with an fp32 output, where a
   // bf16-rounded P would be the dominant error of the result
   constexpr bool PV16 = std::is_same<T, bf16_t>::value && std::is_same<OutT, float>::value;
@@ -303,17 +336,28 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
   // reads in a transposed read fall on distinct banks
   constexpr int LDV = D == 128 ? D + 16 : D + 80;
   __shared__ __attribute__((aligned(16))) union {
-    TP v[kDecWaves][kDecTile * LDV];     // per-wavefront V tile
-    float4 o[kDecWaves][4][D];           // after the tile loop: per-wavefront o, by row quad
+    TP v[W][kDecTile * LDV];             // per-wavefront V tile
+    float4 o[W][4][D];                   // after the tile loop: per-wavefront o, by row quad
     float wt[kDecMaxSplits][kDecRows];   // cross-split merge: weight of each partial
   } sm;
-  __shared__ __attribute__((aligned(16))) float st_m[kDecWaves][kDecRows];
-  __shared__ __attribute__((aligned(16))) float st_l[kDecWaves][kDecRows];
+  __shared__ __attribute__((aligned(16))) float st_m[W][kDecRows];
+  __shared__ __attribute__((aligned(16))) float st_l[W][kDecRows];
   __shared__ int last_s;
+
+  // Every kernel argument in one batch of scalar loads and one wait: left to itself the
+  // compiler loads each where it is first used, three dependent round trips before the cursor
+  // can even be read. The asm takes them all as inputs and passes the split count through to
+  // the workgroup mapping below, so it sits at the top; it is not volatile and touches no
+  // memory, so the metadata reads after it stay scalar loads.
+  asm("" : "+s"(n_splits) : "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.out), "s"(a.lse), "s"(a.kv_len_dev), "s"(a.cu),
+      "s"(a.err), "s"(a.k_new), "s"(a.v_new), "s"(a.cursor), "s"(a.kv_len_out), "s"(ws));
+  asm("" : "+s"(n_splits) : "s"(a.B), "s"(a.Tq), "s"(a.Hq), "s"(a.Hkv), "s"(a.cap), "s"(a.kv_len_host),
+      "s"(a.mask), "s"(a.block), "s"(a.full_cap), "s"(a.scale), "s"(a.scale_log2), "s"(group));
 
   // Workgroup -> (split, b, g). Dispatch deals consecutive workgroup ids to the 8 XCDs in turn;
   // when B*Hkv is a multiple of 8, the ids are arranged so that every split of one (b, g)
-  // lands on the same XCD and its partials meet in one L2.
+  // lands on the same XCD: its partials meet in one L2, and from one step to the next the same
+  // XCD reads the same rows of the head's K/V, which stay in its L2.
   const int BH = a.B * a.Hkv;
   int split, bg;
   if ((BH & 7) == 0) {
@@ -325,7 +369,8 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     bg = blockIdx.x / n_splits;
     split = blockIdx.x - bg * n_splits;
   }
-  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  // (uniform values held in scalar registers: the metadata reads below then stay scalar loads)
+  const int g = __builtin_amdgcn_readfirstlane(bg % a.Hkv), b = __builtin_amdgcn_readfirstlane(bg / a.Hkv);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n16 = lane & 15, G = lane >> 4;
   const int R = a.Tq * group;
@@ -334,44 +379,98 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
   float* ws_o = ws + dec_counter_floats(a.B, a.Hkv);
   float* ws_ml = ws_o + dec_o_floats(a.B, a.Hkv, D, n_splits);
 
-  // query row n16 as the B operand of S^T (independent of the metadata: issued first)
+  // query row n16 as the B operand of S^T (independent of the metadata: issued first).
+  // Rows past R (padding up to the 16-row MFMA block) repeat row R-1: every row has its own
+  // softmax and P V rows, so a repeated row changes no other row, and rows past R are never
+  // written. No lane-divergent branch here: it would turn the uniform values computed around it
+  // into vector registers (and the metadata reads that use them into vector loads), and zeroing
+  // the padding would wait for the query loads before the tile loads go out.
   vec8 qb[DQ];
   {
-    const int r = n16;
-    if (r < R) {
-      const int t = r / group, hh = r - t * group;
-      const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + t) * a.Hq + g * group + hh) * D + 8 * G;
+    const int r = min(n16, R - 1);
+    const int t = r / group, hh = r - t * group;
+    const T* qp = (const T*)a.q + (((int64_t)b * a.Tq + t) * a.Hq + g * group + hh) * D + 8 * G;
 #pragma unroll
-      for (int c = 0; c < DQ; ++c) qb[c] = *(const vec8*)(qp + 32 * c);
-    } else {
-#pragma unroll
-      for (int c = 0; c < DQ; ++c) qb[c] = vec8{};
-    }
+    for (int c = 0; c < DQ; ++c) qb[c] = *(const vec8*)(qp + 32 * c);
   }
 
   // fused step: wave 0 of split 0 copies this head's slice of the new rows into the cache.
   // The sources do not depend on the cursor, so their loads go out here, before the cursor
-  // read; the stores follow once this wave's first tile loads are issued, so neither waits
-  // for the copy. Lane (t, c8): row t, 16-byte granule c8 (Tq * D/8 <= 64 on this path).
+  // read; the stores follow once this wave's tile loads are issued, so neither waits for the
+  // copy. Lane (t, c8): row t, 16-byte granule c8 (Tq * D/8 <= 64 on this path).
   constexpr int VPR = D / 8;
   const int64_t rstride = (int64_t)a.Hkv * D;
   const bool copier = FUSED && split == 0 && wave == 0;  // wave-uniform
   const int cp_t = min(lane / VPR, a.Tq - 1), cp_c8 = lane % VPR;
-  uint4 cpk, cpv;  // set and used only by the copier wave
-  if (copier) {
+  uint4 cpk, cpv;  // set and used only by the copier wave (not with early loads, see below)
+  if (copier && !PATCH) {
     const int64_t src = ((int64_t)b * a.Tq + cp_t) * rstride + (int64_t)g * D + 8 * cp_c8;
     cpk = *(const uint4*)((const T*)a.k_new + src);
     cpv = *(const uint4*)((const T*)a.v_new + src);
   }
+
+  // Tile loads. K: lane (G, n16) takes key tile + n16, d = 32c + 8G .. +8 (the A operand of
+  // S^T). V: lane takes key tile + lane/4, d = 8(4u + lane%4) .. +8 (whole rows per 4 lanes).
+  // Every load is issued unconditionally -- keys past the end read a row that exists (clamped)
+  // and are zeroed where they are used -- so the outstanding loads form a fixed sequence and
+  // the waits before each tile's math cover only that tile.
+  constexpr int LT = DQ + VU;  // loads per tile
+  auto load_rows = [&](const T* kb_, const T* vb_, const T* kn_, const T* vn_, int cur_, int jk,
+                       int jv, uint4* kr, uint4* vr) {
+    const T* kp = (FUSED && jk >= cur_) ? kn_ : kb_;
+#pragma unroll
+    for (int c = 0; c < DQ; ++c) kr[c] = *(const uint4*)(kp + (int64_t)jk * rstride + 32 * c + 8 * G);
+    const T* vp = (FUSED && jv >= cur_) ? vn_ : vb_;
+#pragma unroll
+    for (int u = 0; u < VU; ++u) vr[u] = *(const uint4*)(vp + (int64_t)jv * rstride + 8 * (4 * u + (lane & 3)));
+  };
+
+  // SPEC: the new row in both lane layouts, then the first tile (and with one split the second)
+  // of this wavefront, loaded before the length is known. Rows are clamped to the slab, so every
+  // address is in bounds whatever the length.
+  const int t0s = split * CH + kDecTile * wave;
+  uint4 k0[DQ], v0[VU], k1[DQ], v1[VU];
+  uint4 kn[DQ], vn[VU];  // PATCH only: the new row (Tq = 1) in the K and V lane layouts
+  if constexpr (SPEC) {
+    if constexpr (FUSED) {
+      const int64_t nrow = (int64_t)b * rstride + (int64_t)g * D;  // Tq = 1: row b of k_new
+#pragma unroll
+      for (int c = 0; c < DQ; ++c) kn[c] = *(const uint4*)((const T*)a.k_new + nrow + 32 * c + 8 * G);
+#pragma unroll
+      for (int u = 0; u < VU; ++u) vn[u] = *(const uint4*)((const T*)a.v_new + nrow + 8 * (4 * u + (lane & 3)));
+    }
+    const T* kb0 = (const T*)a.k + (int64_t)b * a.cap * rstride + (int64_t)g * D;
+    const T* vb0 = (const T*)a.v + (int64_t)b * a.cap * rstride + (int64_t)g * D;
+    load_rows(kb0, vb0, nullptr, nullptr, 0x7fffffff, min(t0s + n16, a.cap - 1),
+              min(t0s + (lane >> 2), a.cap - 1), k0, v0);
+    if (n_splits == 1)
+      load_rows(kb0, vb0, nullptr, nullptr, 0x7fffffff, min(t0s + CH + n16, a.cap - 1),
+                min(t0s + CH + (lane >> 2), a.cap - 1), k1, v1);
+  }
+
+  // The copier's stores. With early loads the row is in kn (lane (G, n16) holds granules 4c + G,
+  // c < DQ: lanes 0, 16, 32, 48 cover the row) and vn (lane l < 4 holds granules 4u + l).
   auto copy_new_rows = [&](int cur_, const KeySet& ks_) {
-    if (copier && ks_.ok && lane < a.Tq * VPR) {
+    if (!copier || !ks_.ok) return;
+    if constexpr (PATCH) {
+      T* kd = (T*)a.k + (ks_.base_row + cur_) * rstride + (int64_t)g * D;
+      T* vd = (T*)a.v + (ks_.base_row + cur_) * rstride + (int64_t)g * D;
+      if (n16 == 0) {
+#pragma unroll
+        for (int c = 0; c < DQ; ++c) *(uint4*)(kd + 32 * c + 8 * G) = kn[c];
+      }
+      if (lane < 4) {
+#pragma unroll
+        for (int u = 0; u < VU; ++u) *(uint4*)(vd + 8 * (4 * u + lane)) = vn[u];
+      }
+    } else if (lane < a.Tq * VPR) {
       const int64_t dst = (ks_.base_row + cur_ + cp_t) * rstride + (int64_t)g * D + 8 * cp_c8;
       *(uint4*)((T*)a.k + dst) = cpk;
       *(uint4*)((T*)a.v + dst) = cpv;
     }
   };
 
-  // a rejected batch element still takes part in the arrival count, with empty splits
+  // the key range: a rejected batch element (or a full cache) is one split with no keys
   int cur = 0;  // fused step: the write position of this step
   KeySet ks;
   if constexpr (FUSED) {
@@ -386,11 +485,41 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     ks = key_set(a, b);
     if (!ks.ok && threadIdx.x == 0 && split == 0 && g == 0) report(a.err, dev_error_bit(a));
   }
-  // this split's share of the visited rows, in whole 64-key chunks
+  // this split's share of the visited rows, in whole chunks; splits at or past n_active hold no
+  // keys
   int per = (ks.visit + n_splits - 1) / n_splits;
-  per = (per + kDecChunk - 1) / kDecChunk * kDecChunk;
+  per = (per + CH - 1) / CH * CH;
+  const int n_active = ks.ok ? (ks.visit + per - 1) / per : 1;
   const int start = split * per;
   const int end = ks.ok ? min(ks.visit, start + per) : 0;
+
+  // fused step: every workgroup has read the cursor once it counts itself in here; the count
+  // comes back while the workgroup works and is looked at when it leaves
+  int reader_rank = 0;
+  auto count_reader = [&]() {
+    if constexpr (FUSED) {
+      if (threadIdx.x == 0)
+        reader_rank = __hip_atomic_fetch_add(&counters[BH], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto advance_cursor_if_last_reader = [&]() {
+    if constexpr (FUSED) {
+      if (threadIdx.x == 0 && reader_rank == (int)gridDim.x - 1) {
+        if (ks.ok) {
+          if (a.kv_len_out)
+            for (int bb = 0; bb < a.B; ++bb) a.kv_len_out[bb] = cur + a.Tq;
+          *a.cursor = cur + a.Tq;
+        }
+        __hip_atomic_store(&counters[BH], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  if (split >= n_active) {
+    count_reader();
+    advance_cursor_if_last_reader();
+    return;
+  }
+
   // last visible key of row n16 within this split (padding rows see the whole split)
   int lim = end - 1;
   if (n16 < R) {
@@ -407,22 +536,9 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     knew = (const T*)a.k_new + (int64_t)b * a.Tq * rstride + (int64_t)g * D - (int64_t)cur * rstride;
     vnew = (const T*)a.v_new + (int64_t)b * a.Tq * rstride + (int64_t)g * D - (int64_t)cur * rstride;
   }
-
-  // Tile loads. K: lane (G, n16) takes key tile + n16, d = 32c + 8G .. +8 (the A operand of
-  // S^T). V: lane takes key tile + lane/4, d = 8(4u + lane%4) .. +8 (whole rows per 4 lanes).
-  // Every load is issued unconditionally -- keys at or past `end` read a row that exists
-  // (clamped) and are zeroed after the load -- so the outstanding loads form a fixed sequence
-  // and the waits before each tile's math cover only that tile.
-  constexpr int LT = DQ + VU;  // loads per tile
   auto load_tile = [&](int tile, uint4* kr, uint4* vr) {
-    const int jk = min(tile + n16, max(end - 1, 0));
-    const T* kp = (FUSED && jk >= cur) ? knew : kbase;
-#pragma unroll
-    for (int c = 0; c < DQ; ++c) kr[c] = *(const uint4*)(kp + (int64_t)jk * rstride + 32 * c + 8 * G);
-    const int jv = min(tile + (lane >> 2), max(end - 1, 0));
-    const T* vp = (FUSED && jv >= cur) ? vnew : vbase;
-#pragma unroll
-    for (int u = 0; u < VU; ++u) vr[u] = *(const uint4*)(vp + (int64_t)jv * rstride + 8 * (4 * u + (lane & 3)));
+    load_rows(kbase, vbase, knew, vnew, cur, min(tile + n16, max(end - 1, 0)),
+              min(tile + (lane >> 2), max(end - 1, 0)), kr, vr);
   };
   // Keys at or past `end` count as zero rows. The mask is applied where the tile is used and
   // passes through an empty asm: with a visible condition the compiler would turn the
@@ -433,6 +549,21 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     return k;
   };
   auto masked = [](uint4 x, unsigned k) { return make_uint4(x.x & k, x.y & k, x.z & k, x.w & k); };
+  // PATCH: in an early-loaded tile, key cur (the new row) comes from the k_new/v_new registers
+  // (the tile was read from the cache before this step's row is written). Tiles loaded after the
+  // cursor was read take it from k_new/v_new already.
+  auto pick = [](uint4 x, uint4 y, bool use_y) {
+    return make_uint4(use_y ? y.x : x.x, use_y ? y.y : x.y, use_y ? y.z : x.z, use_y ? y.w : x.w);
+  };
+  auto patch_tile = [&](int tile, uint4* kr, uint4* vr) {
+    if constexpr (PATCH) {
+      const bool new_k = tile + n16 == cur, new_v = tile + (lane >> 2) == cur;
+#pragma unroll
+      for (int c = 0; c < DQ; ++c) kr[c] = pick(kr[c], kn[c], new_k);
+#pragma unroll
+      for (int u = 0; u < VU; ++u) vr[u] = pick(vr[u], vn[u], new_v);
+    }
+  };
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 o[CB];
@@ -448,8 +579,8 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       TP* dst = vt + (lane >> 2) * LDV + 8 * (4 * u + (lane & 3));
+      const uint4 vm = masked(vraw[u], vk);
       if constexpr (PV16) {
-        const uint4 vm = masked(vraw[u], vk);
         const bf16_t* e = (const bf16_t*)&vm;
         typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 h8;
         h8 hv;
@@ -457,20 +588,20 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
         for (int k = 0; k < 8; ++k) hv[k] = (f16_t)(float)e[k];
         *(h8*)dst = hv;
       } else {
-        *(uint4*)dst = masked(vraw[u], vk);
+        *(uint4*)dst = vm;
       }
     }
 
     // S^T = K Q^T: s[j] = score(key tile + 4G + j, row n16)
     f32x4 s = f32x4{};
 #pragma unroll
-    for (int c = 0; c < DQ; ++c) s = MQ::qk(__builtin_bit_cast(vec8, masked(kraw[c], kk)), qb[c], s);
+    for (int c = 0; c < DQ; ++c)
+      s = MQ::qk(__builtin_bit_cast(vec8, masked(kraw[c], kk)), qb[c], s);
     float sv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sv[j] = tile + 4 * G + j <= lim ? s[j] : -INFINITY;
     float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = max_xor32(max_xor16(mt));
     const bool grow = (mt - m) * c2 > kDecRescaleLog2;  // NaN (no move) when both are -inf
     const float m_new = grow ? mt : m;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -510,39 +641,59 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // This wavefront's tiles are t0, t0 + 64, ... below end (wave-uniform). Two tiles ahead:
-  // three register buffers in a loop unrolled by three, so no buffer is copied into another
-  // (a copy would wait for the newest loads), and the 0-2 remaining tiles after the loop.
-  // Before the loop one wait retires everything issued ahead of the first two tiles' loads
-  // (the queries, the new-row write), so the waits the compiler places in the loop count only
-  // tile loads.
+  // This wavefront's tiles are t0, t0 + CH, ... below end (wave-uniform).
   const int t0 = start + kDecTile * wave;
-  const int n_tiles = end > t0 ? (end - t0 + kDecChunk - 1) / kDecChunk : 0;
-  if (n_tiles > 0) {  // then end >= 1 and every clamped row lies in the visited range
-    uint4 k0[DQ], v0[VU], k1[DQ], v1[VU], k2[DQ], v2[VU];
-    load_tile(t0, k0, v0);
-    load_tile(t0 + kDecChunk, k1, v1);
+  const int n_tiles = end > t0 ? (end - t0 + CH - 1) / CH : 0;
+  if (SPEC && per == CH) {
+    // the early tile is this wavefront's only one (t0 == t0s)
+    if constexpr (FUSED) {
+      copy_new_rows(cur, ks);
+      count_reader();
+    }
+    if (n_tiles > 0) {
+      patch_tile(t0, k0, v0);
+      process(t0, k0, v0);
+    }
+  } else if (n_tiles > 0) {  // then end >= 1 and every clamped row lies in the visited range
+    // Two tiles ahead: three register buffers in a loop unrolled by three, so no buffer is
+    // copied into another (a copy would wait for the newest loads), and the 0-2 remaining
+    // tiles after the loop. Before the loop one wait retires everything issued ahead of the
+    // first two tiles' loads (the queries, the new rows' source loads), so the waits the
+    // compiler places in the loop count only tile loads; the copier's stores follow it. With
+    // one split per head the first two tiles were loaded early (t0 == t0s).
+    uint4 k2[DQ], v2[VU];
+    if (!(SPEC && n_splits == 1)) {
+      load_tile(t0, k0, v0);
+      load_tile(t0 + CH, k1, v1);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcntTwoTiles<LT>());
-    if constexpr (FUSED) copy_new_rows(cur, ks);
+    if constexpr (FUSED) {
+      copy_new_rows(cur, ks);
+      count_reader();
+    }
+    if (SPEC && n_splits == 1) {
+      patch_tile(t0, k0, v0);
+      patch_tile(t0 + CH, k1, v1);
+    }
     int i = 0;
     for (; i + 3 <= n_tiles; i += 3) {
-      const int tile = t0 + i * kDecChunk;
-      load_tile(tile + 2 * kDecChunk, k2, v2);
+      const int tile = t0 + i * CH;
+      load_tile(tile + 2 * CH, k2, v2);
       process(tile, k0, v0);
-      load_tile(tile + 3 * kDecChunk, k0, v0);
-      process(tile + kDecChunk, k1, v1);
-      load_tile(tile + 4 * kDecChunk, k1, v1);
-      process(tile + 2 * kDecChunk, k2, v2);
+      load_tile(tile + 3 * CH, k0, v0);
+      process(tile + CH, k1, v1);
+      load_tile(tile + 4 * CH, k1, v1);
+      process(tile + 2 * CH, k2, v2);
     }
-    if (i < n_tiles) process(t0 + i * kDecChunk, k0, v0);
-    if (i + 1 < n_tiles) process(t0 + (i + 1) * kDecChunk, k1, v1);
+    if (i < n_tiles) process(t0 + i * CH, k0, v0);
+    if (i + 1 < n_tiles) process(t0 + (i + 1) * CH, k1, v1);
   } else if constexpr (FUSED) {
     copy_new_rows(cur, ks);  // (the copier wave always has tiles when the step is valid)
+    count_reader();
   }
 
   // row n16's sum: the four lane groups hold different keys of it
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = sum_xor32(sum_xor16(lsum));
   const int RQ = (R + 3) >> 2;  // row quads in use
   __syncthreads();  // every wavefront is done with its V tile: the union becomes the output stage
   if (G == 0) {
@@ -558,11 +709,11 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
   // merge the wavefronts: thread -> (row quad, column)
   const __amdgpu_buffer_rsrc_t ro = ws_rsrc(ws_o, dec_o_floats(a.B, a.Hkv, D, n_splits));
   const __amdgpu_buffer_rsrc_t rml = ws_rsrc(ws_ml, dec_ml_floats(a.B, a.Hkv, n_splits));
-  for (int p = threadIdx.x; p < RQ * D; p += kDecThreads) {
+  for (int p = threadIdx.x; p < RQ * D; p += NT) {
     const int rq = p / D, col = p - rq * D;
-    float4 mw[kDecWaves], lw[kDecWaves], ow[kDecWaves];
+    float4 mw[W], lw[W], ow[W];
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       mw[w] = *(const float4*)&st_m[w][4 * rq];
       lw[w] = *(const float4*)&st_l[w][4 * rq];
       ow[w] = sm.o[w][rq][col];
@@ -572,11 +723,11 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     for (int j = 0; j < 4; ++j) {
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, f4_get(mw[w], j));
+      for (int w = 0; w < W; ++w) M = fmaxf(M, f4_get(mw[w], j));
       const float mu = M == -INFINITY ? 0.f : M;
       float L = 0.f, O = 0.f;
 #pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
+      for (int w = 0; w < W; ++w) {
         const float e = __builtin_amdgcn_exp2f((f4_get(mw[w], j) - mu) * c2);
         L = fmaf(e, f4_get(lw[w], j), L);
         O = fmaf(e, f4_get(ow[w], j), O);
@@ -585,7 +736,7 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
       Lj[j] = L;
       Oj[j] = O;
     }
-    if (n_splits == 1) {  // the workgroup saw every key: its merge is the output
+    if (n_active == 1) {  // the workgroup saw every key: its merge is the output
       float4 v;
       v.x = Lj[0] > 0.f ? Oj[0] / Lj[0] : 0.f;  // L = 0: the batch element was rejected
       v.y = Lj[1] > 0.f ? Oj[1] / Lj[1] : 0.f;
@@ -607,55 +758,45 @@ __global__ void __launch_bounds__(kDecThreads) k_attn_decode(AttnArgs a, int gro
     }
   }
 
-  if (n_splits > 1) {
+  if (n_active > 1) {
     // every store of the workgroup has completed before its arrival is counted
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (threadIdx.x == 0) {
       int* cnt = &counters[b * a.Hkv + g];
       const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = old == n_splits - 1;
+      const bool last = old == n_active - 1;
       if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_s = last;
     }
     __syncthreads();
-    if (!last_s) return;
-    // The partials are read with sc1 loads, the form agent-scope atomic loads take: they see
-    // every store that completed before its workgroup was counted, with no cache invalidate.
-    // The fence keeps the compiler from moving them above the arrival count.
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    merge_splits<D, OutT>(a, group, RQ, ro, rml, sm.wt, b, g, n_splits);
-  }
-  if constexpr (FUSED) {
-    // this workgroup wrote (b, g)'s output; every workgroup of the launch read the cursor
-    // before it got this far, so the last (b, g) to finish may move it (an arrival count
-    // only; no data is handed over)
-    if (threadIdx.x == 0) {
-      const int old = __hip_atomic_fetch_add(&counters[a.B * a.Hkv], 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      if (old == a.B * a.Hkv - 1) {
-        if (ks.ok) {
-          if (a.kv_len_out)
-            for (int bb = 0; bb < a.B; ++bb) a.kv_len_out[bb] = cur + a.Tq;
-          *a.cursor = cur + a.Tq;
-        }
-        __hip_atomic_store(&counters[a.B * a.Hkv], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+    if (last_s) {
+      // The partials are read with sc1 loads, the form agent-scope atomic loads take: they see
+      // every store that completed before its workgroup was counted, with no cache invalidate.
+      // The fence keeps the compiler from moving them above the arrival count.
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      merge_splits<D, OutT, NT>(a, group, RQ, ws_o + dec_o_quad(b, g, 0, 0, a.Hkv, n_splits, D) * 4, rml,
+                                sm.wt, b, g, n_active, n_splits);
     }
   }
+  advance_cursor_if_last_reader();
 }
 
-// Split count used by both the launcher and the workspace query. A split costs one merge
-// round trip, and too few keys per workgroup leave its loads latency-bound: about 128 keys per
-// split, about one workgroup per CU over the chip, and at most 32 splits (fewer, longer splits
-// measured faster from 1K to 32K keys, where the merge of up to 64 partials cost more than the
-// extra parallelism gave).
+// Split count used by both the launcher and the workspace query. Splits are whole chunks
+// (64 keys: one 16-key tile per wavefront), at most one workgroup per CU over the chip and at
+// most 32 per head. When the key bound fits in that many single-chunk splits, each split holds
+// one chunk, so every wavefront's tile is known before the length is read; longer bounds take
+// about 128 keys per split (fewer, longer splits measured faster from 4K to 32K keys, where
+// the merge of many partials cost more than the extra parallelism gave).
 int decode_splits(int B, int Hkv, int max_len) {
-  const int by_len = (max_len + 2 * kDecChunk - 1) / (2 * kDecChunk);
+  constexpr int CH = DecShape<kDecWaves>::chunk;
   int target = 256 / (B * Hkv);
   if (target < 1) target = 1;
-  int s = by_len < target ? by_len : target;
-  if (s > kDecMaxSplits) s = kDecMaxSplits;
+  if (target > kDecMaxSplits) target = kDecMaxSplits;
+  const int one_chunk = (max_len + CH - 1) / CH;
+  if (one_chunk <= target) return one_chunk < 1 ? 1 : one_chunk;
+  const int by_len = (max_len + 2 * CH - 1) / (2 * CH);
+  const int s = by_len < target ? by_len : target;
   return s < 1 ? 1 : s;
 }
 
@@ -664,39 +805,52 @@ size_t decode_workspace_bytes(int B, int Hkv, int D, int n_splits) {
           dec_ml_floats(B, Hkv, n_splits)) * sizeof(float);
 }
 
-template <typename T, int D, typename OutT, bool FUSED>
-static hipError_t launch_decode_f(const AttnArgs& a, int group, float* ws, int n_splits,
-                                  hipStream_t s) {
+template <typename T, int D, typename OutT, bool FUSED, int W>
+static hipError_t launch_decode_w(const AttnArgs& a, int group, float* ws, int n_splits,
+                                  int key_bound, hipStream_t s) {
   const int64_t blocks = (int64_t)n_splits * a.B * a.Hkv;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  dim3 grid((unsigned)blocks), block(kDecThreads);
-  hipLaunchKernelGGL((k_attn_decode<T, D, OutT, FUSED>), grid, block, 0, s, a, group, ws, n_splits);
+  dim3 grid((unsigned)blocks), block(DecShape<W>::threads);
+  // early tile loads: prefix mode, one new row per fused step, and the first tiles' places
+  // fixed by the launch (one chunk per split at the bound, or one split)
+  const bool spec = a.cu == nullptr && (!FUSED || a.Tq == 1) &&
+                    (n_splits == 1 || (int64_t)n_splits * DecShape<W>::chunk >= key_bound);
+  if (spec)
+    hipLaunchKernelGGL((k_attn_decode<T, D, OutT, FUSED, true, W>), grid, block, 0, s, a, group, ws, n_splits);
+  else
+    hipLaunchKernelGGL((k_attn_decode<T, D, OutT, FUSED, false, W>), grid, block, 0, s, a, group, ws, n_splits);
   return hipGetLastError();
+}
+
+template <typename T, int D, typename OutT, bool FUSED>
+static hipError_t launch_decode_f(const AttnArgs& a, int group, float* ws, int n_splits,
+                                  int key_bound, hipStream_t s) {
+  return launch_decode_w<T, D, OutT, FUSED, kDecWaves>(a, group, ws, n_splits, key_bound, s);
 }
 
 template <typename T, int D, typename OutT>
 static hipError_t launch_decode_t(const AttnArgs& a, int group, float* ws, int n_splits,
-                                  hipStream_t s) {
-  return a.cursor ? launch_decode_f<T, D, OutT, true>(a, group, ws, n_splits, s)
-                  : launch_decode_f<T, D, OutT, false>(a, group, ws, n_splits, s);
+                                  int key_bound, hipStream_t s) {
+  return a.cursor ? launch_decode_f<T, D, OutT, true>(a, group, ws, n_splits, key_bound, s)
+                  : launch_decode_f<T, D, OutT, false>(a, group, ws, n_splits, key_bound, s);
 }
 
 hipError_t launch_attn_decode(const AttnArgs& a, int dtype, int out_dtype, int D, void* ws,
-                              int n_splits, hipStream_t s) {
+                              int n_splits, int key_bound, hipStream_t s) {
   const int group = a.Hq / a.Hkv;
   float* w = (float*)ws;
   if (dtype == SKV_BF16) {
     if (D == 128)
-      return out_dtype == SKV_F32 ? launch_decode_t<bf16_t, 128, float>(a, group, w, n_splits, s)
-                                  : launch_decode_t<bf16_t, 128, bf16_t>(a, group, w, n_splits, s);
-    return out_dtype == SKV_F32 ? launch_decode_t<bf16_t, 64, float>(a, group, w, n_splits, s)
-                                : launch_decode_t<bf16_t, 64, bf16_t>(a, group, w, n_splits, s);
+      return out_dtype == SKV_F32 ? launch_decode_t<bf16_t, 128, float>(a, group, w, n_splits, key_bound, s)
+                                  : launch_decode_t<bf16_t, 128, bf16_t>(a, group, w, n_splits, key_bound, s);
+    return out_dtype == SKV_F32 ? launch_decode_t<bf16_t, 64, float>(a, group, w, n_splits, key_bound, s)
+                                : launch_decode_t<bf16_t, 64, bf16_t>(a, group, w, n_splits, key_bound, s);
   }
   if (D == 128)
-    return out_dtype == SKV_F32 ? launch_decode_t<f16_t, 128, float>(a, group, w, n_splits, s)
-                                : launch_decode_t<f16_t, 128, f16_t>(a, group, w, n_splits, s);
-  return out_dtype == SKV_F32 ? launch_decode_t<f16_t, 64, float>(a, group, w, n_splits, s)
-                              : launch_decode_t<f16_t, 64, f16_t>(a, group, w, n_splits, s);
+    return out_dtype == SKV_F32 ? launch_decode_t<f16_t, 128, float>(a, group, w, n_splits, key_bound, s)
+                                : launch_decode_t<f16_t, 128, f16_t>(a, group, w, n_splits, key_bound, s);
+  return out_dtype == SKV_F32 ? launch_decode_t<f16_t, 64, float>(a, group, w, n_splits, key_bound, s)
+                              : launch_decode_t<f16_t, 64, f16_t>(a, group, w, n_splits, key_bound, s);
 }
 
 }  // namespace skv

@@ -73,10 +73,18 @@ struct AttnArgs {
   int32_t* kv_len_out;
 };
 
+// Metadata the kernels only read, through the constant address space: uniform reads of it
+// are then always scalar loads (with the vector loads of the same launch in flight, a vector
+// load of a length would have to wait for all of them).
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int read_meta(const int32_t* p, int i) {
+  return ((const_i32*)p)[i];
+}
+
 __device__ __forceinline__ KeySet key_set(const AttnArgs& a, int b) {
   KeySet s;
   if (a.cu) {
-    int lo = a.cu[b], hi = a.cu[b + 1];
+    int lo = read_meta(a.cu, b), hi = read_meta(a.cu, b + 1);
     // cap is the packed buffer's row count here: a segment may not run past it
     bool ok = (b > 0 || lo == 0) && hi > lo && hi <= a.cap;
     s.base_row = lo;
@@ -84,7 +92,7 @@ __device__ __forceinline__ KeySet key_set(const AttnArgs& a, int b) {
     s.visit = s.len;
     s.ok = ok;
   } else {
-    int len = a.kv_len_dev ? a.kv_len_dev[b] : a.kv_len_host;
+    int len = a.kv_len_dev ? read_meta(a.kv_len_dev, b) : a.kv_len_host;
     bool ok = len >= 1 && len <= a.cap;
     s.base_row = (int64_t)b * a.cap;
     s.len = ok ? len : 0;

@@ -8,9 +8,9 @@ import torch
 
 import seeded_inputs as SI
 from oracle import attention as A
-from tests.helpers import check_attention, f64
+from tests.helpers import bits_equal, check_attention, f64
 
-skv = pytest.importorskip("streaming_kv_cache_write_amd")
+import streaming_kv_cache_write_amd as skv  # noqa: E402  (a missing library fails collection)
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
@@ -57,3 +57,37 @@ def test_decode_merge_reuses_its_workspace():
         o = skv.attn_chunk_fwd(q, k, v, kv_len=kv_len, workspace=ws)
         o_ref, _ = A.attend_batch_prefix(f64(q), f64(k), f64(v), [kv_len] * B, A.MASK_NONE, 1)
         check_attention(o, o_ref, "bf16", f"kv_len {kv_len}")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_lengths_below_and_past_the_bound(fused):
+    """The split grid is sized from max_seqlen_kv (256 keys: four one-chunk splits, whose
+    tiles are loaded before the length is read). Shorter lengths leave splits empty; they
+    leave at once and the merge reads only the others. A device length past the bound makes
+    every split longer than one chunk: the early tiles are dropped and the splits loaded
+    again. Every step is checked against the oracle."""
+    B, Hq, Hkv, D, cap, bound = 1, 32, 8, 128, 2048, 256
+    q = SI.per_batch_normal(B, (1, Hq, D), "misc", "q", chunk=47, dtype="bf16").to(DEV)
+    k = SI.per_batch_normal(B, (cap, Hkv, D), "misc", "k", chunk=47, dtype="bf16").to(DEV)
+    v = SI.per_batch_normal(B, (cap, Hkv, D), "misc", "v", chunk=47, dtype="bf16").to(DEV)
+    ws = torch.zeros(skv.attn_workspace_bytes(q, k, kv_len=bound), dtype=torch.uint8, device=DEV)
+    kv_len = torch.zeros(B, dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    for L in (1, 63, 64, 65, 130, 255, 256, 257, 700, 2048):
+        if fused:
+            kc, vc = k.clone(), v.clone()
+            cursor = torch.full((1,), L - 1, dtype=torch.int32, device=DEV)
+            o = skv.attn_decode_step(q, k[:, L - 1:L].contiguous(), v[:, L - 1:L].contiguous(), kc, vc,
+                                     cursor, kv_len_out=kv_len, max_seqlen_kv=bound, workspace=ws, err=err)
+            torch.cuda.synchronize()
+            assert int(cursor) == L and kv_len.tolist() == [L]
+            assert bits_equal(kc, k) and bits_equal(vc, v)
+        else:
+            kv_len.fill_(L)
+            o = skv.attn_chunk_fwd(q, k, v, kv_len_dev=kv_len, max_seqlen_kv=bound, workspace=ws, err=err)
+        o_ref, _ = A.attend_batch_prefix(qf, kf, vf, [L], A.MASK_NONE, 1)
+        check_attention(o, o_ref, "bf16", f"kv_len {L} fused {fused}")
+    torch.cuda.synchronize()
+    assert int(err) == 0
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0  # arrival counters back at zero
