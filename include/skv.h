@@ -280,6 +280,9 @@ typedef struct {
   int32_t* err_dev;                 /* optional device error word */
 } skv_attn_params;
 
+/* Bytes of workspace a call with these parameters needs (0: none); (size_t)-1 when the
+   parameters are invalid (the status attn_chunk_fwd would return is then described by
+   skv_last_error()). */
 size_t attn_workspace_bytes(const skv_attn_params* params);
 skv_status attn_chunk_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
                           const skv_attn_params* params, void* stream);

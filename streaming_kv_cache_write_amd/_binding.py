@@ -115,6 +115,56 @@ def _dev_tensor(t, name: str, dtype=None):
     return t
 
 
+def _shape(t, shape, name: str):
+    """Shape check before any C call: the C ABI takes raw pointers, so a tensor whose size does
+    not match the sizes passed with it would be read or written out of bounds on the device."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _ndim(t, n: int, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions (got shape {tuple(t.shape)})")
+    return t.shape
+
+
+def _numel(t, n: int, name: str, at_least: bool = False):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if (t.numel() < n) if at_least else (t.numel() != n):
+        raise ValueError(f"{name} has {t.numel()} elements, expected {'at least ' if at_least else ''}{n}")
+    return t
+
+
+# One zero-filled workspace per (device, stream), grown on demand, for calls that do not bring
+# their own: calls on one stream are ordered, and each leaves the workspace's arrival counters
+# at zero for the next. Calls recorded into a HIP graph get a fresh one (allocated from the
+# graph's pool); callers that replay graphs or run concurrent streams pass their own.
+_WORKSPACES: dict = {}
+
+
+def _workspace(device, need: int):
+    if need <= 0:
+        return None
+    if torch.cuda.is_current_stream_capturing():
+        return torch.zeros(need, dtype=torch.uint8, device=device)
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def dtype_code(dtype: torch.dtype) -> int:
     if dtype not in _DTYPES:
         raise TypeError(f"unsupported dtype {dtype}")
@@ -124,8 +174,14 @@ def dtype_code(dtype: torch.dtype) -> int:
 # ------------------------------------------------------------------------------ writes
 def kv_write_indexed(k_cache, v_cache, k_src, v_src, index=None, start: int = 0, err=None):
     """k_cache[b, index[t]] = k_src[b, t] (and V); index None -> rows start .. start+n."""
+    B, cap, Hkv, D = _ndim(k_cache, 4, "k_cache")
+    n = _ndim(k_src, 4, "k_src")[1]
+    _shape(k_src, (B, n, Hkv, D), "k_src")
+    _shape(v_cache, k_cache.shape, "v_cache")
+    _shape(v_src, k_src.shape, "v_src")
+    _numel(index, n, "index")
+    _numel(err, 1, "err", at_least=True)
     _dev_tensor(k_cache, "k_cache")
-    B, cap, Hkv, D = k_cache.shape
     _dev_tensor(k_src, "k_src", k_cache.dtype)
     if v_cache is not None:
         _dev_tensor(v_cache, "v_cache", k_cache.dtype)
@@ -151,8 +207,14 @@ def kv_write_indexed_rope(k_cache, v_cache, k_src, v_src, inv_freq, rope_layout:
                           index=None, start: int = 0, err=None):
     """kv_write_indexed with K rotated at its destination row: inv_freq float64 [D/2] on the
     device, rope_layout ROPE_HALF or ROPE_INTERLEAVED."""
+    B, cap, Hkv, D = _ndim(k_cache, 4, "k_cache")
+    n = _ndim(k_src, 4, "k_src")[1]
+    _shape(k_src, (B, n, Hkv, D), "k_src")
+    _shape(v_cache, k_cache.shape, "v_cache")
+    _shape(v_src, k_src.shape, "v_src")
+    _numel(index, n, "index")
+    _numel(err, 1, "err", at_least=True)
     _dev_tensor(k_cache, "k_cache")
-    B, cap, Hkv, D = k_cache.shape
     _dev_tensor(k_src, "k_src", k_cache.dtype)
     if v_cache is not None:
         _dev_tensor(v_cache, "v_cache", k_cache.dtype)
@@ -171,6 +233,9 @@ def kv_write_indexed_rope(k_cache, v_cache, k_src, v_src, inv_freq, rope_layout:
 
 def kv_cursor_advance(cursor, n: int, cap: int, index_out, kv_len_out=None, err=None):
     """index_out[t] = cursor + t, kv_len_out[:] = cursor + n, cursor += n, all on the device."""
+    _numel(cursor, 1, "cursor", at_least=True)
+    _numel(index_out, int(n), "index_out")
+    _numel(err, 1, "err", at_least=True)
     _dev_tensor(cursor, "cursor", torch.int32)
     _dev_tensor(index_out, "index_out", torch.int64)
     B = 0
@@ -186,8 +251,9 @@ def kv_cursor_advance(cursor, n: int, cap: int, index_out, kv_len_out=None, err=
 def kv_roll_left(k_store, v_store, sink_rows: int, shift_rows: int):
     """Move rows [sink_rows + shift_rows, rows) of k_store/v_store [B, rows, Hkv, D] to
     [sink_rows, rows - shift_rows) (memmove semantics): the chronological window's roll-left."""
+    B, rows, Hkv, D = _ndim(k_store, 4, "k_store")
+    _shape(v_store, k_store.shape, "v_store")
     _dev_tensor(k_store, "k_store")
-    B, rows, Hkv, D = k_store.shape
     if v_store is not None:
         _dev_tensor(v_store, "v_store", k_store.dtype)
     _check(lib.kv_roll_left(_ptr(k_store), _ptr(v_store), B, rows, int(sink_rows), int(shift_rows),
@@ -196,8 +262,10 @@ def kv_roll_left(k_store, v_store, sink_rows: int, shift_rows: int):
 
 def kv_ragged_metadata(lens, max_kv: int, cu_seqlens_out=None, err=None):
     """cu_seqlens_kv [B+1] int32 (exclusive prefix sums of lens [B] int32), on the device."""
-    _dev_tensor(lens, "lens", torch.int32)
     B = lens.numel()
+    _numel(cu_seqlens_out, B + 1, "cu_seqlens_out")
+    _numel(err, 1, "err", at_least=True)
+    _dev_tensor(lens, "lens", torch.int32)
     if cu_seqlens_out is None:
         cu_seqlens_out = torch.empty(B + 1, dtype=torch.int32, device=lens.device)
     _dev_tensor(cu_seqlens_out, "cu_seqlens_out", torch.int32)
@@ -213,8 +281,13 @@ def kv_ragged_metadata(lens, max_kv: int, cu_seqlens_out=None, err=None):
 def kv_pack_ragged(k_padded, v_padded, cu_seqlens, k_packed, v_packed=None, err=None):
     """Rows [0, len_b) of k_padded/v_padded [B, max_kv, Hkv, D] to rows [cu[b], cu[b+1]) of
     k_packed/v_packed [packed_rows, Hkv, D], len_b = cu[b+1] - cu[b]."""
+    B, max_kv, Hkv, D = _ndim(k_padded, 4, "k_padded")
+    _shape(v_padded, k_padded.shape, "v_padded")
+    _shape(k_packed, (_ndim(k_packed, 3, "k_packed")[0], Hkv, D), "k_packed")
+    _shape(v_packed, k_packed.shape, "v_packed")
+    _numel(cu_seqlens, B + 1, "cu_seqlens")
+    _numel(err, 1, "err", at_least=True)
     _dev_tensor(k_padded, "k_padded")
-    B, max_kv, Hkv, D = k_padded.shape
     _dev_tensor(k_packed, "k_packed", k_padded.dtype)
     if v_padded is not None:
         _dev_tensor(v_padded, "v_padded", k_padded.dtype)
@@ -231,8 +304,9 @@ class Ring:
     """Sink-plus-window ring over caller storage k_store/v_store [B, n_slots*chunk, Hkv, D]."""
 
     def __init__(self, k_store, v_store, chunk: int, n_slots: int, sink_slots: int, meta=None):
+        B, rows, Hkv, D = _ndim(k_store, 4, "k_store")
+        _shape(v_store, k_store.shape, "v_store")
         _dev_tensor(k_store, "k_store")
-        B, rows, Hkv, D = k_store.shape
         if rows != n_slots * chunk:
             raise ValueError(f"storage has {rows} rows, expected n_slots*chunk = {n_slots * chunk}")
         if v_store is not None:
@@ -255,11 +329,20 @@ class Ring:
         return self._h.value
 
     def reserve(self, batch_mask=None):
+        _numel(batch_mask, self.B, "batch_mask")
         if batch_mask is not None:
             _dev_tensor(batch_mask, "batch_mask", torch.uint8)
         _check(lib.kv_ring_reserve(self._h, _ptr(batch_mask), _stream(self.k_store.device)))
 
+    def _check_sources(self, k_src, v_src, batch_mask, err):
+        _, _, Hkv, D = self.k_store.shape
+        _shape(k_src, (self.B, self.chunk, Hkv, D), "k_src")
+        _shape(v_src, k_src.shape, "v_src")
+        _numel(batch_mask, self.B, "batch_mask")
+        _numel(err, 1, "err", at_least=True)
+
     def write(self, k_src, v_src=None, batch_mask=None, err=None):
+        self._check_sources(k_src, v_src, batch_mask, err)
         _dev_tensor(k_src, "k_src", self.k_store.dtype)
         if v_src is not None:
             _dev_tensor(v_src, "v_src", self.k_store.dtype)
@@ -275,6 +358,7 @@ class Ring:
     def write_rope(self, k_src, v_src, inv_freq, rope_layout: int = ROPE_HALF, batch_mask=None,
                    err=None):
         """write() with K rotated at chunk_id * chunk + t (chunk_id since the last reset)."""
+        self._check_sources(k_src, v_src, batch_mask, err)
         _dev_tensor(k_src, "k_src", self.k_store.dtype)
         if v_src is not None:
             _dev_tensor(v_src, "v_src", self.k_store.dtype)
@@ -290,6 +374,7 @@ class Ring:
                                       _stream(self.k_store.device)))
 
     def reset(self, batch_mask=None):
+        _numel(batch_mask, self.B, "batch_mask")
         if batch_mask is not None:
             _dev_tensor(batch_mask, "batch_mask", torch.uint8)
         _check(lib.kv_ring_reset(self._h, _ptr(batch_mask), _stream(self.k_store.device)))
@@ -348,8 +433,38 @@ def make_params(q, k, *, kv_len=None, kv_len_dev=None, cu_seqlens_kv=None, max_s
     return p
 
 
+SIZE_INVALID = ctypes.c_size_t(-1).value  # attn_workspace_bytes of an invalid parameter set
+
+
+def _workspace_need(q, k, **kw) -> int:
+    """Workspace bytes for these parameters, or 0 if they are invalid (the call itself then
+    returns the precise status)."""
+    n = int(lib.attn_workspace_bytes(ctypes.byref(make_params(q, k, **kw))))
+    return 0 if n == SIZE_INVALID else n
+
+
 def attn_workspace_bytes(q, k, **kw) -> int:
-    return int(lib.attn_workspace_bytes(ctypes.byref(make_params(q, k, **kw))))
+    """Workspace bytes a call with these arguments needs; ValueError if they are invalid."""
+    n = int(lib.attn_workspace_bytes(ctypes.byref(make_params(q, k, **kw))))
+    if n == SIZE_INVALID:
+        raise ValueError(f"invalid attention parameters: {lib.skv_last_error().decode()}")
+    return n
+
+
+def _check_attn_shapes(q, k, v, out, lse, kv_len_dev, cu_seqlens_kv, err):
+    B, Tq, Hq, D = _ndim(q, 4, "q")
+    if cu_seqlens_kv is not None and kv_len_dev is not None:
+        return  # an unsupported combination: the library refuses it before any launch
+    if cu_seqlens_kv is not None:
+        _shape(k, (_ndim(k, 3, "k")[0], k.shape[1], D), "k")
+        _numel(cu_seqlens_kv, B + 1, "cu_seqlens_kv")
+    else:
+        _shape(k, (B, _ndim(k, 4, "k")[1], k.shape[2], D), "k")
+    _shape(v, k.shape, "v")
+    _shape(out, q.shape, "out")
+    _shape(lse, (B, Hq, Tq), "lse")
+    _numel(kv_len_dev, B, "kv_len_dev")
+    _numel(err, 1, "err", at_least=True)
 
 
 def attn_chunk_fwd(q, k, v, out=None, lse=None, *, kv_len=None, kv_len_dev=None,
@@ -357,7 +472,9 @@ def attn_chunk_fwd(q, k, v, out=None, lse=None, *, kv_len=None, kv_len_dev=None,
                    full_capacity_masked=False, out_dtype=None, workspace=None, err=None):
     """Attention of q [B, Tq, Hq, D] over k/v [B, cap, Hkv, D] (prefix: host kv_len or device
     kv_len_dev [B] int32) or packed k/v [total, Hkv, D] (cu_seqlens_kv [B+1] int32).
-    Returns out [B, Tq, Hq, D] (and fills lse [B, Hq, Tq] fp32 if given)."""
+    Returns out [B, Tq, Hq, D] (and fills lse [B, Hq, Tq] fp32 if given). Without a workspace
+    the call uses the one cached for its device and stream (see _workspace)."""
+    _check_attn_shapes(q, k, v, out, lse, kv_len_dev, cu_seqlens_kv, err)
     _dev_tensor(q, "q")
     _dev_tensor(k, "k", q.dtype)
     _dev_tensor(v, "v", q.dtype)
@@ -377,9 +494,7 @@ def attn_chunk_fwd(q, k, v, out=None, lse=None, *, kv_len=None, kv_len_dev=None,
               max_seqlen_kv=max_seqlen_kv, mask=mask, mask_block=mask_block, scale=scale,
               full_capacity_masked=full_capacity_masked, out_dtype=odt, err=err)
     if workspace is None:
-        need = attn_workspace_bytes(q, k, **kw)
-        if need:  # zero-filled: the split-K arrival counters must start at zero
-            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(q.device, _workspace_need(q, k, **kw))
     if workspace is not None:
         _dev_tensor(workspace, "workspace")
     p = make_params(q, k, workspace=workspace, **kw)
@@ -393,7 +508,18 @@ def attn_decode_step(q, k_new, v_new, k_cache, v_cache, cursor, out=None, lse=No
                      out_dtype=None, workspace=None, err=None):
     """One fused decode step: write k_new/v_new [B, Tq, Hkv, D] at the device cursor, attend q
     [B, Tq, Hq, D] over the cache prefix including them, advance the cursor (and fill
-    kv_len_out [B]). Returns out."""
+    kv_len_out [B]). Returns out. Without a workspace the call uses the cached one."""
+    B, Tq, Hq, D = _ndim(q, 4, "q")
+    _, cap, Hkv, _ = _ndim(k_cache, 4, "k_cache")
+    _shape(k_cache, (B, cap, Hkv, D), "k_cache")
+    _shape(v_cache, k_cache.shape, "v_cache")
+    _shape(k_new, (B, Tq, Hkv, D), "k_new")
+    _shape(v_new, (B, Tq, Hkv, D), "v_new")
+    _shape(out, q.shape, "out")
+    _shape(lse, (B, Hq, Tq), "lse")
+    _numel(cursor, 1, "cursor", at_least=True)
+    _numel(kv_len_out, B, "kv_len_out")
+    _numel(err, 1, "err", at_least=True)
     _dev_tensor(q, "q")
     for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
         _dev_tensor(t, name, q.dtype)
@@ -408,12 +534,12 @@ def attn_decode_step(q, k_new, v_new, k_cache, v_cache, cursor, out=None, lse=No
     _dev_tensor(out, "out", odt)
     if lse is not None:
         _dev_tensor(lse, "lse", torch.float32)
-    bound = int(max_seqlen_kv) if max_seqlen_kv else k_cache.shape[1]
+    bound = int(max_seqlen_kv) if max_seqlen_kv else cap
     kw = dict(max_seqlen_kv=max_seqlen_kv, mask=mask, mask_block=mask_block, scale=scale,
               out_dtype=odt, err=err)
     if workspace is None:
-        need = attn_workspace_bytes(q, k_cache, kv_len=min(bound, k_cache.shape[1]), **kw)
-        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+        need = _workspace_need(q, k_cache, kv_len=max(min(bound, cap), Tq), **kw)
+        workspace = _workspace(q.device, max(need, 16))
     _dev_tensor(workspace, "workspace")
     p = make_params(q, k_cache, workspace=workspace, **kw)
     _check(lib.attn_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),

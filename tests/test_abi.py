@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "skv.h")
 
-skv = pytest.importorskip("streaming_kv_cache_write_amd")
+import streaming_kv_cache_write_amd as skv  # noqa: E402  (a missing library fails collection)
 lib = skv.lib
 
 
@@ -97,8 +97,13 @@ def test_valid_kv_len_bounds_pass_validation_of_workspace_query():
     for kv_len in (1, 64):
         assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=kv_len))) > 0
     assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=8))) == 0
-    assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=0))) == 0
-    assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=65))) == 0
+    # invalid parameters: a distinct result, never mistaken for "no workspace needed"
+    invalid = ctypes.c_size_t(-1).value
+    assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=0))) == invalid
+    assert "kv_len" in lib.skv_last_error().decode()
+    assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=65))) == invalid
+    assert lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, D=96))) == invalid
+    assert lib.attn_workspace_bytes(None) == invalid
     # the split-K workspace grows with the longest prefix it may see
     small = lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=64, cap=64)))
     large = lib.attn_workspace_bytes(ctypes.byref(params(Tq=1, kv_len=4096, cap=4096)))

@@ -14,7 +14,7 @@ import seeded_inputs as SI
 from oracle import attention as A
 from tests.helpers import bits_equal, check_attention, f64
 
-skv = pytest.importorskip("streaming_kv_cache_write_amd")
+import streaming_kv_cache_write_amd as skv  # noqa: E402  (a missing library fails collection)
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}

@@ -3,7 +3,7 @@ than a workgroup's span), and the MFMA probe runs to completion with finite outp
 import pytest
 import torch
 
-skv = pytest.importorskip("streaming_kv_cache_write_amd")
+import streaming_kv_cache_write_amd as skv  # noqa: E402  (a missing library fails collection)
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 

@@ -15,7 +15,7 @@ from oracle import cache as Cc
 from oracle import rope as R
 from tests.helpers import check_attention, f64
 
-skv = pytest.importorskip("streaming_kv_cache_write_amd")
+import streaming_kv_cache_write_amd as skv  # noqa: E402  (a missing library fails collection)
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TD = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}

@@ -14,6 +14,8 @@
 
 Large inputs are drawn on the device (seeded torch generator); the oracle receives copies of
 those inputs, never anything the library produced."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,9 +23,10 @@ import torch
 import seeded_inputs as SI
 from oracle import attention as A
 from oracle import cache as Cc
+from oracle import rope as R
 from tests.helpers import bits_equal, check_attention, f64
 
-skv = pytest.importorskip("streaming_kv_cache_write_amd")
+import streaming_kv_cache_write_amd as skv  # noqa: E402  (a missing library fails collection)
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TD = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
@@ -36,6 +39,18 @@ def _bits(t):
 
 def _from_bits(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).view(TD[dtype])
+
+
+def _rope_keys_bf16_bits(k, positions, inv):
+    """oracle.rope.rope_keys of k [B, T, H, D] (bf16 tensor) as bf16 bits, the heads split over
+    threads (numpy releases the GIL inside its large array operations)."""
+    from concurrent.futures import ThreadPoolExecutor
+    kf = f64(k)
+    H = kf.shape[2]
+    parts = [slice(h, min(h + 2, H)) for h in range(0, H, 2)]
+    with ThreadPoolExecutor(max_workers=min(len(parts), os.cpu_count() or 1, 16)) as ex:
+        rot = list(ex.map(lambda sl: R.rope_keys(kf[:, :, sl], positions, inv, R.LAYOUT_HALF, "bf16"), parts))
+    return _bits(torch.from_numpy(np.concatenate(rot, axis=2)).to(torch.bfloat16))
 
 
 # ----------------------------------------------------------------------------------- tiny
@@ -146,6 +161,10 @@ def test_ring_sequence_full_size():
     sims_v = [Cc.RingPhysical(W.n_slots, W.sink, W.C, (W.H, W.D), dtype=np.int16) for _ in range(W.B)]
     rng = np.random.default_rng(3)
     got, want = [], []
+    # keys rotated at their absolute positions as they are written (the workload's RoPE-before-
+    # write); the simulated storage holds the oracle's rotation of the same inputs
+    inv = 10000.0 ** (-np.arange(W.D // 2) * 2.0 / W.D)
+    inv_dev = torch.from_numpy(inv).to(DEV)
     plan = [(0, c) for c in range(W.n_chunks)] + [("reset", None)] + [(1, c) for c in range(2)]
     for seg, c in plan:
         if seg == "reset":
@@ -164,9 +183,17 @@ def test_ring_sequence_full_size():
             q = SI.per_batch_device_normal(W.B, shape, "ring", "q", DEV, "bf16", chunk=chunk_id, rewrite=r)
             k = SI.per_batch_device_normal(W.B, shape, "ring", "k", DEV, "bf16", chunk=chunk_id, rewrite=r)
             v = SI.per_batch_device_normal(W.B, shape, "ring", "v", DEV, "bf16", chunk=chunk_id, rewrite=r)
-            ring.write(k, v, err=err)
+            ring.write_rope(k, v, inv_dev, rope_layout=skv.ROPE_HALF, err=err)
             o = skv.attn_chunk_fwd(q, k_store, v_store, kv_len_dev=ring.kv_len, max_seqlen_kv=rows)
-            kb, vb = _bits(k), _bits(v)
+            heads = [int(rng.integers(W.H)) for _ in range(W.B)]
+            pos = R.ring_positions(c, W.C)
+            vb = _bits(v)
+            if r == W.rewrites - 1:  # the retained rewrite: every head, for the storage compare
+                kb = _rope_keys_bf16_bits(k, pos, inv)
+            else:  # only the head the attention check samples (the others are rewritten later)
+                kb = _bits(k).copy()
+                for b, h in enumerate(heads):
+                    kb[b, :, h:h + 1] = _rope_keys_bf16_bits(k[b:b + 1, :, h:h + 1], pos, inv)[0]
             for b in range(W.B):
                 sims_k[b].write(kb[b])
                 sims_v[b].write(vb[b])
@@ -177,7 +204,7 @@ def test_ring_sequence_full_size():
             # sampled rows (two (b, h) pairs x 192 queries, first and last query included)
             # against the oracle over the simulated storage, which was built from the inputs
             for b in range(W.B):
-                h = int(rng.integers(W.H))
+                h = heads[b]
                 ts = np.unique(np.concatenate([[0, W.C - 1], rng.integers(W.C, size=190)]))
                 L = lens[b]
                 kk = f64(_from_bits(sims_k[b].storage[:L, h:h + 1], "bf16"))

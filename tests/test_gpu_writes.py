@@ -12,7 +12,7 @@ import seeded_inputs as SI
 from oracle import cache as Cc
 from tests.helpers import bits_equal
 
-skv = pytest.importorskip("streaming_kv_cache_write_amd")
+import streaming_kv_cache_write_amd as skv  # noqa: E402  (a missing library fails collection)
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
@@ -215,3 +215,77 @@ def test_ring_independent_branches_with_batch_mask():
         for b in range(B):
             assert np.array_equal(g[b], sims[b].storage)
             assert int(ring.kv_len[b]) == sims[b].valid_tokens()
+
+
+def test_reset_recovers_after_a_flagged_bad_write():
+    """Failure recovery with the ring's own primitive: after a write the device refuses (the
+    cond branch wrote without a reservation: SKV_DEV_RING_UNRESERVED, that branch untouched),
+    kv_ring_reset of that branch brings it back to a state from which every further write,
+    wraparound included, matches the oracle's physical ring bit for bit, and attention over
+    the recovered ring matches the oracle over the same storage."""
+    from oracle import attention as A
+    from tests.helpers import check_attention, f64
+    B, C, n_slots, sink, Hkv, Hq, D = 2, 16, 4, 1, 2, 4, 64
+    k_store = torch.zeros(B, n_slots * C, Hkv, D, dtype=torch.bfloat16, device=DEV)
+    v_store = torch.zeros_like(k_store)
+    ring = skv.Ring(k_store, v_store, C, n_slots, sink)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sims_k = [Cc.RingPhysical(n_slots, sink, C, (Hkv, D), dtype=np.int16) for _ in range(B)]
+    sims_v = [Cc.RingPhysical(n_slots, sink, C, (Hkv, D), dtype=np.int16) for _ in range(B)]
+    only1 = torch.tensor([0, 1], dtype=torch.uint8, device=DEV)
+    only0 = torch.tensor([1, 0], dtype=torch.uint8, device=DEV)
+
+    def chunk(i):
+        ks = SI.per_batch_normal(B, (C, Hkv, D), "misc", "k", chunk=60 + i, dtype="bf16")
+        vs = SI.per_batch_normal(B, (C, Hkv, D), "misc", "v", chunk=60 + i, dtype="bf16")
+        return ks, vs
+
+    def step(i, mask, active):
+        ring.reserve(mask)
+        ks, vs = chunk(i)
+        ring.write(ks.to(DEV), vs.to(DEV), batch_mask=mask, err=err)
+        kb, vb = _np_bits(ks), _np_bits(vs)
+        for b in active:
+            sims_k[b].reserve(), sims_v[b].reserve()
+            sims_k[b].write(kb[b]), sims_v[b].write(vb[b])
+
+    def compare(what):
+        torch.cuda.synchronize()
+        gk, gv = _np_bits(k_store), _np_bits(v_store)
+        for b in range(B):
+            assert np.array_equal(gk[b], sims_k[b].storage), (what, b)
+            assert np.array_equal(gv[b], sims_v[b].storage), (what, b)
+            assert int(ring.kv_len[b]) == sims_k[b].valid_tokens(), (what, b)
+
+    for i in range(3):
+        step(i, None, [0, 1])
+    compare("before the fault")
+    # the fault: branch 0 is reset, then written with no reservation (only branch 1 reserved)
+    ring.reset(only0)
+    for s in (sims_k[0], sims_v[0]):
+        s.reset()
+    ring.reserve(only1)
+    ks, vs = chunk(3)
+    ring.write(ks.to(DEV), vs.to(DEV), err=err)
+    for s, x in ((sims_k[1], ks), (sims_v[1], vs)):
+        s.reserve()
+        s.write(_np_bits(x)[1])
+    compare("after the refused write")
+    assert int(err) == skv.DEV_RING_UNRESERVED
+    # recovery: reset the faulted branch, clear the error word, carry on past a wraparound
+    err.zero_()
+    ring.reset(only0)
+    for s in (sims_k[0], sims_v[0]):
+        s.reset()
+    for i in range(4, 4 + 2 * n_slots):
+        step(i, None, [0, 1])
+        compare(f"recovered step {i}")
+    assert int(err) == 0
+    q = SI.per_batch_normal(B, (C, Hq, D), "misc", "q", chunk=99, dtype="bf16")
+    o = skv.attn_chunk_fwd(q.to(DEV), k_store, v_store, kv_len_dev=ring.kv_len, max_seqlen_kv=n_slots * C)
+    lens = ring.kv_len.tolist()
+    def oracle_store(sim):  # the oracle's own storage (bf16 bits), not the GPU's
+        return f64(torch.from_numpy(np.ascontiguousarray(sim.storage)).view(torch.bfloat16))
+    refs = np.stack([A.attend_prefix(f64(q[b]), oracle_store(sims_k[b]), oracle_store(sims_v[b]), lens[b])[0]
+                     for b in range(B)])
+    check_attention(o, refs, "bf16", "attention over the recovered ring")
