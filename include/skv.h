@@ -309,6 +309,28 @@ skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new,
                             int32_t* kv_len_out_dev, const skv_attn_params* params, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Fused decode step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): attn_decode_step with the
+ * split-K scratch (arrival counters and partials) in a static array the library holds on each
+ * GPU it runs on, SKV_DECODE_STATIC_SCRATCH_BYTES per GPU, kept until the process ends.
+ *
+ * Arguments, results and device errors are those of attn_decode_step; params->workspace and
+ * params->workspace_bytes are ignored. A step whose scratch need (attn_workspace_bytes() of
+ * the same parameters; it grows with B*Hkv and the key bound) exceeds
+ * SKV_DECODE_STATIC_SCRATCH_BYTES returns SKV_ERR_RANGE and launches nothing. The call
+ * allocates nothing; its first call on a GPU looks up that GPU's array (that device must be
+ * current) and clears its counters with a kernel on `stream`, and every call leaves them
+ * cleared. All calls on one GPU share its array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and give undefined
+ * results; calls issued on one stream are ordered.
+ * ------------------------------------------------------------------------------------ */
+#define SKV_DECODE_STATIC_SCRATCH_BYTES (4u << 20)
+skv_status attn_decode_step_static(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                   void* v_cache, void* out, float* lse, int32_t* cursor_dev,
+                                   int32_t* kv_len_out_dev, const skv_attn_params* params,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Measurement probes (not part of the hot path): ceilings measured on the chip by kernels of
  * this library, against which the hot-path kernels are also reported (the nominal peaks of
  * the data sheet assume a 2.4 GHz clock the chip does not hold under matrix-core load).

@@ -80,6 +80,8 @@ _SIGS = {
     "attn_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, ctypes.POINTER(skv_attn_params), _vp]),
     "attn_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                               ctypes.POINTER(skv_attn_params), _vp]),
+    "attn_decode_step_static": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     ctypes.POINTER(skv_attn_params), _vp]),
     "skv_probe_mfma_bf16": (_i, [_vp, _i, _i, _vp]),
     "skv_probe_copy": (_i, [_vp, _vp, _sz, _vp]),
 }
@@ -505,10 +507,12 @@ def attn_chunk_fwd(q, k, v, out=None, lse=None, *, kv_len=None, kv_len_dev=None,
 
 def attn_decode_step(q, k_new, v_new, k_cache, v_cache, cursor, out=None, lse=None, *,
                      kv_len_out=None, max_seqlen_kv=0, mask=MASK_NONE, mask_block=1, scale=0.0,
-                     out_dtype=None, workspace=None, err=None):
+                     out_dtype=None, workspace=None, err=None, static_scratch=False):
     """One fused decode step: write k_new/v_new [B, Tq, Hkv, D] at the device cursor, attend q
     [B, Tq, Hq, D] over the cache prefix including them, advance the cursor (and fill
-    kv_len_out [B]). Returns out. Without a workspace the call uses the cached one."""
+    kv_len_out [B]). Returns out. Without a workspace the call uses the cached one;
+    static_scratch=True calls attn_decode_step_static instead (no workspace at all; out must
+    then be given for the call to allocate nothing)."""
     B, Tq, Hq, D = _ndim(q, 4, "q")
     _, cap, Hkv, _ = _ndim(k_cache, 4, "k_cache")
     _shape(k_cache, (B, cap, Hkv, D), "k_cache")
@@ -537,6 +541,12 @@ def attn_decode_step(q, k_new, v_new, k_cache, v_cache, cursor, out=None, lse=No
     bound = int(max_seqlen_kv) if max_seqlen_kv else cap
     kw = dict(max_seqlen_kv=max_seqlen_kv, mask=mask, mask_block=mask_block, scale=scale,
               out_dtype=odt, err=err)
+    if static_scratch:
+        p = make_params(q, k_cache, **kw)
+        _check(lib.attn_decode_step_static(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                           _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(cursor),
+                                           _ptr(kv_len_out), ctypes.byref(p), _stream(q.device)))
+        return out
     if workspace is None:
         need = _workspace_need(q, k_cache, kv_len=max(min(bound, cap), Tq), **kw)
         workspace = _workspace(q.device, max(need, 16))

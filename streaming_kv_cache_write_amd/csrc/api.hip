@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -426,9 +427,16 @@ skv_status attn_chunk_fwd(const void* q, const void* k, const void* v, void* out
   return fail(SKV_ERR_UNSUPPORTED, "no path");
 }
 
-skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
-                            void* v_cache, void* out, float* lse, int32_t* cursor_dev,
-                            int32_t* kv_len_out_dev, const skv_attn_params* p, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both fused decode entry points; on success *splits and *bound hold the launch
+// plan and *need the workspace bytes it takes.
+skv_status check_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                             void* v_cache, void* out, float* lse, int32_t* cursor_dev,
+                             int32_t* kv_len_out_dev, const skv_attn_params* p, int* splits,
+                             int* bound, size_t* need) {
   if (!p) return fail(SKV_ERR_NULL, "params is NULL");
   if (!k_new || !v_new || !cursor_dev) return fail(SKV_ERR_NULL, "k_new, v_new and cursor_dev must be non-NULL");
   if (p->kv_len_dev || p->cu_seqlens_kv_dev || (p->flags & SKV_FULL_CAPACITY_MASKED))
@@ -439,21 +447,22 @@ skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new,
   if (v.mask != SKV_MASK_NONE && v.Tq > v.kv_len) v.kv_len = v.Tq;
   skv_status st = validate_attn(q, k_cache, v_cache, out, &v);
   if (st != SKV_OK) return st;
-  if (p->Tq == 0) return ok();
-  if (choose_path(v) != PATH_DECODE)
+  if (p->Tq > 0 && choose_path(v) != PATH_DECODE)
     return fail(SKV_ERR_UNSUPPORTED, "the fused decode step needs bf16/f16, Tq <= %d, "
                 "Tq*Hq/Hkv <= %d and B*Hkv < %d", kDecodeMaxTq, kDecodeMaxRows, kWsCounterInts);
   if (!aligned16(k_new) || !aligned16(v_new) || ((uintptr_t)cursor_dev & 3) ||
       ((uintptr_t)kv_len_out_dev & 3) || (lse && ((uintptr_t)lse & 3)))
     return fail(SKV_ERR_ALIGN, "misaligned k_new / v_new / cursor / kv_len_out / lse");
-  v.kv_len_dev = nullptr;
-  const int bound = p->max_seqlen_kv > 0 && p->max_seqlen_kv < p->cap ? p->max_seqlen_kv : p->cap;
-  const int splits = decode_splits(p->B, p->Hkv, bound);
-  const size_t need = decode_workspace_bytes(p->B, p->Hkv, p->D, splits);
-  if (!p->workspace) return fail(SKV_ERR_NULL, "the decode step needs a workspace of %zu bytes", need);
-  if (p->workspace_bytes < need)
-    return fail(SKV_ERR_RANGE, "workspace of %zu bytes < %zu required", p->workspace_bytes, need);
-  if (!aligned16(p->workspace)) return fail(SKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  *bound = p->max_seqlen_kv > 0 && p->max_seqlen_kv < p->cap ? p->max_seqlen_kv : p->cap;
+  *splits = decode_splits(p->B, p->Hkv, *bound);
+  *need = decode_workspace_bytes(p->B, p->Hkv, p->D, *splits);
+  return SKV_OK;
+}
+
+skv_status launch_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, void* out, float* lse, int32_t* cursor_dev,
+                              int32_t* kv_len_out_dev, const skv_attn_params* p, void* ws,
+                              int splits, int bound, hipStream_t stream, const char* what) {
   AttnArgs a{};
   a.q = q;
   a.k = k_cache;
@@ -474,9 +483,96 @@ skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new,
   a.v_new = v_new;
   a.cursor = cursor_dev;
   a.kv_len_out = kv_len_out_dev;
-  return hip_status(launch_attn_decode(a, p->dtype, p->out_dtype, p->D, p->workspace, splits,
-                                       bound, (hipStream_t)stream),
-                    "attn_decode_step launch");
+  return hip_status(launch_attn_decode(a, p->dtype, p->out_dtype, p->D, ws, splits, bound, stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+skv_status attn_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                            void* v_cache, void* out, float* lse, int32_t* cursor_dev,
+                            int32_t* kv_len_out_dev, const skv_attn_params* p, void* stream) {
+  int splits = 0, bound = 0;
+  size_t need = 0;
+  skv_status st = check_decode_step(q, k_new, v_new, k_cache, v_cache, out, lse, cursor_dev,
+                                    kv_len_out_dev, p, &splits, &bound, &need);
+  if (st != SKV_OK) return st;
+  if (p->Tq == 0) return ok();
+  if (!p->workspace) return fail(SKV_ERR_NULL, "the decode step needs a workspace of %zu bytes", need);
+  if (p->workspace_bytes < need)
+    return fail(SKV_ERR_RANGE, "workspace of %zu bytes < %zu required", p->workspace_bytes, need);
+  if (!aligned16(p->workspace)) return fail(SKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return launch_decode_step(q, k_new, v_new, k_cache, v_cache, out, lse, cursor_dev, kv_len_out_dev, p,
+                            p->workspace, splits, bound, (hipStream_t)stream, "attn_decode_step launch");
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused decode step without a caller workspace
+// ---------------------------------------------------------------------------------------
+}  // extern "C"
+
+// The split-K scratch of attn_decode_step_static: arrival counters (the first kWsCounterInts
+// ints, zero between calls) and partials. Each GPU the library runs on holds its own copy
+// until the process ends. In host code `scratch` is only a stand-in for the symbol: the device
+// address of this GPU's copy comes from hipGetSymbolAddress and is the only form used.
+static __device__ __align__(256) unsigned char scratch[SKV_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kStaticScratchBytes = SKV_DECODE_STATIC_SCRATCH_BYTES;
+
+__global__ void k_zero_ints(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once set up
+
+// This device's scratch address; the first call on a device looks it up (with that device
+// current) and clears the counter area by a kernel on `stream` (not a memset, which a graph
+// capture would record as a memset node).
+skv_status device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SKV_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    hipLaunchKernelGGL(k_zero_ints, dim3(64), dim3(256), 0, stream, (int*)ptr, kWsCounterInts);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "clearing the static scratch");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+skv_status attn_decode_step_static(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                   void* v_cache, void* out, float* lse, int32_t* cursor_dev,
+                                   int32_t* kv_len_out_dev, const skv_attn_params* p, void* stream) {
+  int splits = 0, bound = 0;
+  size_t need = 0;
+  skv_status st = check_decode_step(q, k_new, v_new, k_cache, v_cache, out, lse, cursor_dev,
+                                    kv_len_out_dev, p, &splits, &bound, &need);
+  if (st != SKV_OK) return st;
+  if (need > kStaticScratchBytes)
+    return fail(SKV_ERR_RANGE, "this decode step needs %zu bytes of split-K scratch; the static scratch "
+                "holds %zu (B*Hkv and the key bound set the need)", need, kStaticScratchBytes);
+  if (p->Tq == 0) return ok();
+  void* ws = nullptr;
+  st = device_scratch((hipStream_t)stream, &ws);
+  if (st != SKV_OK) return st;
+  return launch_decode_step(q, k_new, v_new, k_cache, v_cache, out, lse, cursor_dev, kv_len_out_dev, p,
+                            ws, splits, bound, (hipStream_t)stream, "attn_decode_step_static launch");
 }
 
 // ---------------------------------------------------------------------------------------

@@ -278,3 +278,16 @@ def test_probe_host_errors():
     assert c(P, P, 24, None) == skv.SKV_ERR_SHAPE
     assert c(BAD, P, 16, None) == skv.SKV_ERR_ALIGN
     assert c(P, P, 0, None) == skv.SKV_OK  # nothing to do, nothing launched
+
+
+def test_static_scratch_decode_step_host_errors():
+    """attn_decode_step_static refuses, before touching the GPU, a step whose split-K scratch
+    would not fit the static array, and shares the fused step's other host checks."""
+    f = lib.attn_decode_step_static
+    # q, k_new, v_new, k_cache, v_cache, out, lse, cursor, kv_len_out, params, stream
+    big = params(Tq=1, kv_len=32768, cap=32768, B=64, Hq=64, Hkv=8)
+    assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(big), None) == skv.SKV_ERR_RANGE
+    assert "static scratch" in lib.skv_last_error().decode()
+    assert f(P, None, P, P, P, P, None, P, None, ctypes.byref(big), None) == skv.SKV_ERR_NULL
+    packed = params(Tq=1, kv_len=64, cap=64, cu_seqlens_kv_dev=P)
+    assert f(P, P, P, P, P, P, None, P, None, ctypes.byref(packed), None) == skv.SKV_ERR_UNSUPPORTED
