@@ -14,6 +14,8 @@ Bars (written here once, used by every parity test):
 """
 from __future__ import annotations
 
+import warnings
+
 import numpy as np
 import torch
 
@@ -61,3 +63,13 @@ def bits_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
     ia = a.contiguous().view(torch.uint8)
     ib = b.contiguous().view(torch.uint8)
     return bool(torch.equal(ia, ib))
+
+
+class AgreementReport(UserWarning):
+    """Measured parity figures of a workload test, shown in pytest's warnings summary (which a
+    quiet run still prints) so that a passing run records them too."""
+
+
+def report(what: str, stats: dict) -> None:
+    parts = [f"{k}={v:.6g}" if isinstance(v, float) else f"{k}={v}" for k, v in stats.items()]
+    warnings.warn(f"{what}: " + " ".join(parts), AgreementReport, stacklevel=2)

@@ -24,7 +24,7 @@ import seeded_inputs as SI
 from oracle import attention as A
 from oracle import cache as Cc
 from oracle import rope as R
-from tests.helpers import bits_equal, check_attention, f64
+from tests.helpers import bits_equal, check_attention, f64, report
 
 import streaming_kv_cache_write_amd as skv  # noqa: E402  (a missing library fails collection)
 pytestmark = pytest.mark.gpu
@@ -146,7 +146,7 @@ def test_decode_prefill_and_1024_steps(dtype):
     stats = check_attention(outs, refs, dtype, "decode steps")
     for i, o in full_arm.items():
         check_attention(o[0, 0], refs[i], dtype, f"full-capacity arm step {i}")
-    print(f"decode {dtype}: {stats}")
+    report(f"decode job {dtype}", stats)
 
 
 # ----------------------------------------------------------------------------------- ring
@@ -222,7 +222,7 @@ def test_ring_sequence_full_size():
             assert np.array_equal(gv[b], sims_v[b].storage), (seg, c, b)
     assert int(err) == 0
     stats = check_attention(np.concatenate(got), np.concatenate(want), "bf16", "ring, all sampled rows")
-    print(f"ring: {stats}")
+    report("ring sequence", stats)
 
 
 # ---------------------------------------------------------------------------- multi-user
@@ -261,7 +261,7 @@ def test_multiuser_block_causal_full_size():
     torch.cuda.synchronize()
     assert int(err) == 0 and kv_len.tolist() == [W.cap] * W.B
     stats = check_attention(np.concatenate(got), np.concatenate(want), "bf16", "multi-user, all sampled rows")
-    print(f"multi-user: {stats}")
+    report("multi-user sequence", stats)
     for b in (0, W.B - 1):
         ref_k = np.zeros((1, W.cap, W.H, W.D), dtype=np.int16)
         for c in range(W.n_chunks):
@@ -302,4 +302,4 @@ def test_ragged_cross_attention_full_size(lens):
         got.append(f64(o_p[b, tsd, h:h + 1]))
         want.append(ref)
     stats = check_attention(np.concatenate(got), np.concatenate(want), "bf16", f"ragged {lens}")
-    print(f"ragged {lens}: {stats}")
+    report(f"ragged {lens}", stats)
