@@ -340,7 +340,37 @@ def bench_ring(torch, skv, SI, dev):
                 skv.kv_write_indexed(ks, vs, k, v, start=filled - W.C)
                 skv.attn_chunk_fwd(q, ks, vs, out, kv_len=filled, workspace=ws)
 
+    def clone_rolling_sequence():
+        # the same arm with the page's roll as written there: clone the retained non-sink rows,
+        # then copy them back one chunk to the left (torch copies; twice the bytes of the
+        # in-place roll, and a temporary as large as the moved rows)
+        filled = 0
+        for c in range(W.n_chunks):
+            if filled + W.C > rows:
+                lo = W.sink * W.C
+                for st in (ks, vs):
+                    kept = st[:, lo + W.C:].clone()
+                    st[:, lo:rows - W.C].copy_(kept)
+                    del kept
+            else:
+                filled += W.C
+            for r in range(W.rewrites):
+                q, k, v = srcs[(c % 2) * 2 + (r % 2)]
+                skv.kv_write_indexed(ks, vs, k, v, start=filled - W.C)
+                skv.attn_chunk_fwd(q, ks, vs, out, kv_len=filled, workspace=ws)
+
+    def peak_mb(fn):
+        """Peak device memory allocated through torch while fn runs (storage included)."""
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        fn()
+        torch.cuda.synchronize()
+        return torch.cuda.max_memory_allocated() / 1e6
+
     roll_seq_ms = time_gpu(torch, rolling_sequence, reps=3, warm=1)
+    clone_seq_ms = time_gpu(torch, clone_rolling_sequence, reps=3, warm=1)
+    peak = {"ring_sequence_mb": peak_mb(sequence), "inplace_roll_sequence_mb": peak_mb(rolling_sequence),
+            "clone_roll_sequence_mb": peak_mb(clone_rolling_sequence)}
     # saturated step: 7 valid slots
     ring.reset()
     for c in range(W.n_slots):
@@ -354,6 +384,14 @@ def bench_ring(torch, skv, SI, dev):
     flush = make_flush(torch, dev)
     write_ms = time_gpu(torch, lambda: ring.write(srcs[0][1], srcs[0][2]), reps=10, flush=flush)
     roll_ms = time_gpu(torch, lambda: skv.kv_roll_left(ks, vs, W.sink * W.C, W.C), reps=10, flush=flush)
+
+    def clone_roll():
+        lo = W.sink * W.C
+        for st in (ks, vs):
+            kept = st[:, lo + W.C:].clone()
+            st[:, lo:rows - W.C].copy_(kept)
+
+    clone_roll_ms = time_gpu(torch, clone_roll, reps=10, flush=flush)
     # keys rotated at their absolute positions before storage: fused into the ring write, and
     # the unfused path (a separate rotation by torch in fp32, then the plain write) beside it
     half = W.D // 2
@@ -419,11 +457,17 @@ def bench_ring(torch, skv, SI, dev):
             "vs_plain_write": rope_ms / write_ms},
         "rolling_arm": {
             "what": "chronological buffer with roll-left past the sink (the path the ring replaces): "
-                    "same chunk lifecycle, host kv_len",
+                    "same chunk lifecycle, host kv_len; in place (kv_roll_left, ordered chunk-sized "
+                    "copies) and as the page writes it (clone the retained rows, copy them back)",
             "sequence_ms": roll_seq_ms, "vs_ring_sequence": roll_seq_ms / seq_ms,
             "roll_ms_cold": roll_ms, "roll_rows_moved": moved, "roll_bytes": rbytes,
             "roll_gbs": rbytes / roll_ms * 1e-6, "rolls_per_sequence": n_rolls,
-            "ring_maintenance_bytes": 0},
+            "clone_then_copy": {"sequence_ms": clone_seq_ms, "vs_ring_sequence": clone_seq_ms / seq_ms,
+                                "roll_ms_cold": clone_roll_ms, "roll_bytes": 2 * rbytes,
+                                "roll_gbs": 2 * rbytes / clone_roll_ms * 1e-6,
+                                "temporary_mb": rbytes / 2 / 2 / 1e6},
+            "ring_maintenance_bytes": 0,
+            "peak_allocated_mb": peak},
     }
 
 
@@ -606,43 +650,76 @@ def bench_peaks(torch, skv, SI, dev, rows):
 
 
 # ----------------------------------------------------------------------------------------
-# CPU baseline: the fp64 oracle on a bounded sample of the decode job
+# CPU baseline: the fp64 oracle on the host cores (a reported baseline, not a target)
 # ----------------------------------------------------------------------------------------
-def cpu_baseline(SI, dtype, n_steps=300):
-    import numpy as np
-    from oracle import attention as A
-    from oracle import cache as Cc
-    W = SI.Decode()
-    n = W.prompt + n_steps
-    q = SI.as_f64(SI.per_batch_normal(1, (n, W.Hq, W.D), "decode", "q", std=W.std, dtype=dtype))[0]
-    k = SI.as_f64(SI.per_batch_normal(1, (n, W.Hkv, W.D), "decode", "k", std=W.std, dtype=dtype))
-    v = SI.as_f64(SI.per_batch_normal(1, (n, W.Hkv, W.D), "decode", "v", std=W.std, dtype=dtype))
-    T = W.prompt
-    t0 = time.perf_counter()
-    kc, _ = Cc.slab_write_indexed(np.zeros((1, W.cap, W.Hkv, W.D)), k[:, :T], np.arange(T))
-    vc, _ = Cc.slab_write_indexed(np.zeros((1, W.cap, W.Hkv, W.D)), v[:, :T], np.arange(T))
-    A.attend_prefix(q[:T], kc[0], vc[0], T, A.MASK_CAUSAL)
-    for i in range(n_steps):
-        kc, _ = Cc.slab_write_indexed(kc, k[:, T + i:T + i + 1], [T + i])
-        vc, _ = Cc.slab_write_indexed(vc, v[:, T + i:T + i + 1], [T + i])
-        A.attend_prefix(q[T + i:T + i + 1], kc[0], vc[0], T + i + 1)
-    secs = time.perf_counter() - t0
-    kv_bytes = 2 * T * W.Hkv * W.D * ELEM + sum(2 * (T + i + 1) * W.Hkv * W.D * ELEM for i in range(n_steps))
+def _host_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         import threadpoolctl
         threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    return model, threads
+
+
+def _median_of(fn, runs=3):
+    """Median wall time of `runs` timed calls after one untimed warm call."""
+    fn()
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times), times
+
+
+def cpu_baseline(SI, dtype):
+    """The fp64 oracle's attention over the whole decode job (234-token causal prefill and all
+    1024 single-token steps, kv_len 235 .. 1258), median of 3 warm runs. The oracle's caches
+    are built once beforehand, untimed: its slab write copies the capacity-sized cache on every
+    call, which would time numpy copies rather than attention; attend_prefix reads only rows
+    [0, kv_len) of them. Bytes are the job's K/V bytes at 2 B per element, as for the GPU."""
+    import numpy as np
+    from oracle import attention as A
+    from oracle import cache as Cc
+    W = SI.Decode()
+    n = W.prompt + W.steps
+    q = SI.as_f64(SI.per_batch_normal(1, (n, W.Hq, W.D), "decode", "q", std=W.std, dtype=dtype))[0]
+    k = SI.as_f64(SI.per_batch_normal(1, (n, W.Hkv, W.D), "decode", "k", std=W.std, dtype=dtype))
+    v = SI.as_f64(SI.per_batch_normal(1, (n, W.Hkv, W.D), "decode", "v", std=W.std, dtype=dtype))
+    kc, _ = Cc.slab_write_indexed(np.zeros((1, W.cap, W.Hkv, W.D)), k, np.arange(n))
+    vc, _ = Cc.slab_write_indexed(np.zeros((1, W.cap, W.Hkv, W.D)), v, np.arange(n))
+    T = W.prompt
+
+    def job():
+        A.attend_prefix(q[:T], kc[0], vc[0], T, A.MASK_CAUSAL)
+        for i in range(W.steps):
+            A.attend_prefix(q[T + i:T + i + 1], kc[0], vc[0], T + i + 1)
+
+    secs, runs = _median_of(job)
+    kv_bytes = 2 * T * W.Hkv * W.D * ELEM + sum(2 * (T + i + 1) * W.Hkv * W.D * ELEM for i in range(W.steps))
+    model, threads = _host_info()
     return {"value": kv_bytes / secs / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": secs, "host_cpus": os.cpu_count(),
-            "sample": f"prefill (234-token causal) + first {n_steps} of 1024 decode steps, "
-                      f"fp64 numpy oracle incl. its slab writes (capacity 32768)"}
+            "seconds": secs, "runs": len(runs), "run_seconds": [round(x, 4) for x in runs],
+            "statistic": "median of 3 warm runs", "cpu_model": model, "host_cpus": os.cpu_count(),
+            "blas_threads": threads,
+            "sample": "the whole decode job: fp64 numpy oracle attention for the 234-token causal "
+                      "prefill and all 1024 decode steps (caches built beforehand, untimed)"}
 
 
 def cpu_baseline_rows(SI):
-    """The fp64 oracle on bounded samples of the other workloads (a few seconds in all):
-    attention over a sample of query rows of one (b, h) at the workload's key count, and one
-    cache write of the workload's size. Rates are per sample and so per query row."""
+    """The fp64 oracle on the other workloads (median of 3 warm runs each, ~10 s in all): the
+    tiny fp32 workload whole; attention over a sample of query rows of one (b, h) at each
+    workload's key count (rates per query row scale linearly to the whole workload, which is
+    rows x heads x batch times larger); one cache write of each workload's size."""
     import numpy as np
     from oracle import attention as A
     from oracle import cache as Cc
@@ -653,29 +730,46 @@ def cpu_baseline_rows(SI):
         q = rng.standard_normal((n_q, 1, D))
         k = rng.standard_normal((L, 1, D))
         v = rng.standard_normal((L, 1, D))
-        t0 = time.perf_counter()
         allowed = np.stack([A.visible_keys(Tq - n_q + i, Tq, L, mask) for i in range(n_q)])
-        A.attend_keys(q, k, v, allowed)
-        secs = time.perf_counter() - t0
+        secs, _ = _median_of(lambda: A.attend_keys(q, k, v, allowed))
         flop = 4 * D * int(allowed.sum())
-        return {"tflops": flop / secs * 1e-12, "seconds": round(secs, 3),
+        return {"tflops": flop / secs * 1e-12, "seconds": round(secs, 4),
                 "sample": f"{n_q} query rows x {L} keys, one head"}
 
     def write_rate(rows, H, D, fn):
         src = rng.standard_normal((1, rows, H, D))
-        t0 = time.perf_counter()
-        fn(src)
-        secs = time.perf_counter() - t0
-        return {"gbs": 2 * src.size * ELEM / secs * 1e-9, "seconds": round(secs, 3),
+        secs, _ = _median_of(lambda: fn(src))
+        return {"gbs": 2 * src.size * ELEM / secs * 1e-9, "seconds": round(secs, 4),
                 "sample": f"{rows} rows x {H} heads x {D}, bytes counted at 2 B per element"}
 
+    def tiny_whole():
+        W = SI.Tiny()
+        qs = SI.as_f64(SI.per_batch_normal(W.B, (W.chunk * W.n_chunks, W.H, W.D), "tiny", "q"))
+        ks = SI.as_f64(SI.per_batch_normal(W.B, (W.chunk * W.n_chunks, W.H, W.D), "tiny", "k"))
+        vs = SI.as_f64(SI.per_batch_normal(W.B, (W.chunk * W.n_chunks, W.H, W.D), "tiny", "v"))
+
+        def run():
+            kc = np.zeros((W.B, W.cap, W.H, W.D))
+            vc = np.zeros_like(kc)
+            for c in range(W.n_chunks):
+                idx = np.arange(W.chunk * c, W.chunk * (c + 1))
+                kc, _ = Cc.slab_write_indexed(kc, ks[:, idx], idx)
+                vc, _ = Cc.slab_write_indexed(vc, vs[:, idx], idx)
+                A.attend_batch_prefix(qs[:, idx], kc, vc, [W.chunk * (c + 1)] * W.B)
+
+        secs, _ = _median_of(run)
+        return {"seconds": round(secs, 5), "us_per_chunk_step": secs / W.n_chunks * 1e6,
+                "sample": "the whole tiny workload: B=2, 7 chunks of 8 tokens (writes + attention)"}
+
     R, M, G = SI.Ring(), SI.MultiUser(), SI.Ragged()
-    attn_rate(64, 4096, 128)  # warm-up: BLAS threads
-    res = {"what": "fp64 numpy oracle on samples of the other workloads, host cores as in cpu_baseline"}
+    model, threads = _host_info()
+    res = {"what": "fp64 numpy oracle, median of 3 warm runs each", "cpu_model": model,
+           "blas_threads": threads}
+    res["tiny_workload"] = tiny_whole()
     res["ring_saturated_attention"] = attn_rate(256, R.n_slots * R.C, R.D)
     res["multiuser_chunk15_attention"] = attn_rate(256, M.cap, M.D, A.MASK_BLOCK_CAUSAL, Tq=M.chunk)
     for L0, L1 in G.skews:
-        res[f"ragged_{L0}_{L1}_attention"] = attn_rate(8192, L1, G.D)
+        res[f"ragged_{L0}_{L1}_attention"] = attn_rate(4096, L1, G.D)
     ring = Cc.RingPhysical(R.n_slots, R.sink, R.C, (R.H, R.D))
     ring.reserve()
     res["ring_write"] = write_rate(R.C, R.H, R.D, lambda s: ring.write(s[0]))
@@ -780,6 +874,18 @@ def main():
             line["measured_peaks"] = {"error": repr(e)}
         torch.cuda.empty_cache()
         line["rows"] = rows
+        ring, mu = rows.get("ring", {}), rows.get("multiuser", {})
+        line["chunk_attention"] = {
+            "what": "the metric's chunk-attention part: bf16 TFLOP/s of the saturated ring step (7 "
+                    "valid slots, 4680 queries over 32760 keys, B=2, 12 heads) and of multi-user chunk 15 "
+                    "(1024 queries over 16384 keys causal in chunk, B=8, 40 heads), fraction of the "
+                    "2516.6 TFLOP/s peak; ms per chunk step of both sequences (write + attention)",
+            "ring_saturated_tflops": ring.get("saturated_attn_tflops"),
+            "ring_saturated_frac_mfma": ring.get("saturated_attn_frac_mfma"),
+            "multiuser_chunk15_tflops": mu.get("chunk15_attn_tflops"),
+            "multiuser_chunk15_frac_mfma": mu.get("chunk15_attn_frac_mfma"),
+            "ring_ms_per_rewrite_step": ring.get("ms_per_rewrite_step"),
+            "multiuser_ms_per_chunk_step": mu.get("ms_per_chunk_step")}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(SI, args.dtype)
         if not args.no_rows:
