@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libskv.so")
+# SKV_LIBRARY names another build of the same library: the CPU ABI tests load the host-side
+# AddressSanitizer build through it; it is never a fallback.
+LIB_PATH = os.environ.get("SKV_LIBRARY") or os.path.join(_HERE, "libskv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python streaming_kv_cache_write_amd/build.py`")
