@@ -34,10 +34,11 @@
 //   * Workgroup ids are remapped so the query tiles of one (b, h) run on the same XCD and
 //     share its L2 copy of K/V (dispatch hands consecutive workgroup ids to the 8 XCDs in turn),
 //     with the (b, h) pairs dealt round-robin over the XCDs so unequal heads stay balanced.
-//   * Q and O cross global memory as whole rows: Q is loaded 16 bytes per lane in row order
-//     and moved into the operand layout through LDS in the prologue; each wavefront's
-//     normalised output block is staged in an idle tile buffer and stored 4 rows per
-//     instruction (the operand and accumulator layouts would touch 32 rows per instruction).
+//   * Q and O cross global memory as whole rows: Q goes straight into LDS like a K tile (in
+//     the two tile buffers idle until tile 1) and is read from there once in the operand
+//     layout; each wavefront's normalised output block is staged in an idle tile buffer and
+//     stored 4 rows per instruction (the operand and accumulator layouts would touch 32 rows
+//     per instruction).
 //   * Tail split (optional, needs a workspace): when the last round of workgroups would leave
 //     many of the CU slots idle, the items of that round are cut by key range into a few
 //     pieces. Each piece stores its unnormalised O^T, reference max and row sums; the last
@@ -69,6 +70,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // is kept: probabilities stay below 2^8, far inside bf16/fp16 range, O needs no rescale, and the
 // final O / l and lse are unchanged because numerator and denominator share the reference.
 constexpr float kRescaleLog2 = 8.f;
+
+// Workgroup barrier over LDS only: the wavefront's LDS operations have completed, while its
+// global loads and stores stay in flight (__syncthreads would also drain those).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt fields left at their maxima)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -177,7 +182,17 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
   // to the 8 XCDs in turn; the (b, h) pairs are dealt to the XCDs the same way (XCD x takes
   // bh = x, x + 8, ...), each with all its query tiles in order, so a head's K/V is shared in
   // one L2 and heads of unequal cost (ragged batch elements) spread over every XCD.
-  const int bid = blockIdx.x, BH = a.B * a.Hq, n_qtiles = fg.n_qtiles;
+  // Every kernel argument in one batch of scalar loads and one wait (left to itself the
+  // compiler loads each where it is first used: three dependent round trips before the first
+  // query loads go out). The asm takes them all as inputs and passes the tile count through to
+  // the mapping below; it is not volatile and touches no memory, so the metadata reads after
+  // it stay scalar loads.
+  int n_qtiles = fg.n_qtiles;
+  asm("" : "+s"(n_qtiles) : "s"(a.q), "s"(a.k), "s"(a.v), "s"(a.out), "s"(a.lse), "s"(a.kv_len_dev), "s"(a.cu),
+      "s"(a.err), "s"(fg.ws), "s"(fg.nf), "s"(fg.r), "s"(fg.parts));
+  asm("" : "+s"(n_qtiles) : "s"(a.B), "s"(a.Tq), "s"(a.Hq), "s"(a.Hkv), "s"(a.cap), "s"(a.kv_len_host),
+      "s"(a.mask), "s"(a.block), "s"(a.full_cap), "s"(a.scale), "s"(a.scale_log2), "s"(gridDim.x));
+  const int bid = blockIdx.x, BH = a.B * a.Hq;
   int qt, bh, part = 0, split_id = -1;
   if ((BH & 7) == 0) {
     int k = bid >> 3;
@@ -200,45 +215,43 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int g = h / (a.Hq / a.Hkv);
+  const int tid = threadIdx.x;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // (the wavefront index as a scalar: the buffer resources built from it stay in scalar
+  // registers, with no loop over distinct per-lane values around each load and store)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int my_q = qt * kFlashBM + wave * 32 + l32;
   const bool q_ok = my_q < a.Tq;
-  OutT* out_row = (OutT*)a.out + (((int64_t)b * a.Tq + my_q) * a.Hq + h) * D;
-
-  // this wave's queries, the B operand of S^T = K Q^T, loaded once. They need no key
-  // metadata, so they go out first and their latency overlaps the metadata read and the
-  // first K/V loads. The loads read whole rows (RPI rows of 16-byte granules per
-  // instruction, instead of 32 rows x 32 bytes in the operand layout); the prologue
-  // rearranges them through LDS.
-  // Rows past Tq lie outside the load resource's range and read as zeros, so every load is
-  // unconditional (per-row branches made the compiler wait for the first load to land).
-  constexpr int RPI = 64 / GPR;  // query rows per load instruction
   const int q0 = qt * kFlashBM + wave * 32;  // first query row of this wavefront
+  const int n_qrows = __builtin_amdgcn_readfirstlane(max(min(32, a.Tq - q0), 0));  // (scalar)
+
+  // This wave's 32 queries, the B operand of S^T = K Q^T, go from global memory straight into
+  // LDS (Ks1 holds the rows of waves 0-1, Vs1 those of waves 2-3; both are idle until tile 1's
+  // loads), laid out and swizzled like a K tile, and are read from there once in the operand
+  // layout. Rows past Tq lie outside the load resource's range and read as zeros.
   const int row_stride = a.Hq * D * (int)sizeof(T);  // host-checked: 32 rows fit an int
-  const int n_qrows = max(min(32, a.Tq - q0), 0);
-  vec qraw[DC], qreg[DC];
+  constexpr int QP = 32 * ROWB / 1024;  // 1 KB pieces of a wavefront's query rows
+  unsigned char* const q_lds = (wave < 2 ? Ks1 : Vs1) + (wave & 1) * 32 * ROWB;
   {
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const T*)a.q + (((int64_t)b * a.Tq + q0) * a.Hq + h) * D), (short)0,
         n_qrows > 0 ? (n_qrows - 1) * row_stride + D * (int)sizeof(T) : 0, kBufferRsrcWord3);
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const int row = c * RPI + lane / GPR;
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, row * row_stride + 16 * (lane % GPR), 0, 0);
-      __builtin_memcpy(&qraw[c], &x, 16);
+    for (int pc = 0; pc < QP; ++pc) {
+      const int r = pc * RPC + lane / GPR;  // row of the wave's 32; (wave & 1) * 32 + r in the buffer
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (__attribute__((address_space(3))) void*)(q_lds + pc * 1024), 16,
+          (int)(r * row_stride + 16 * ((lane % GPR) ^ sk((wave & 1) * 32 + r))), 0, 0, 0);
     }
   }
 
+  vec qreg[DC];
+
+  // An invalid length (reported once per launch) leaves the workgroup no tiles: it runs the
+  // same path as an empty key set and writes zero rows with lse = -inf.
   const KeySet ks = key_set(a, b);
-  if (!ks.ok) {  // uniform over the workgroup
-    if (q_ok)
-      for (int d = 4 * hi; d < D; d += 8) store4<OutT>(out_row + d, 0.f, 0.f, 0.f, 0.f);
-    if (q_ok && a.lse && hi == 0) a.lse[((int64_t)b * a.Hq + h) * a.Tq + my_q] = -INFINITY;
-    if (tid == 0 && qt == 0 && h == 0) report(a.err, dev_error_bit(a));
-    return;
-  }
+  if (!ks.ok && tid == 0 && qt == 0 && h == 0) report(a.err, dev_error_bit(a));
 
   // key range: the workgroup's last query bounds it; keys below key_full are visible to
   // every query of the workgroup, so those tiles need no mask at all
@@ -248,9 +261,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
   const int key_end = a.full_cap ? ks.visit : row_limit(a.mask, a.block, q_last + shift, ks.len) + 1;
   const int key_full = row_limit(a.mask, a.block, q_first + shift, ks.len) + 1;
   int my_lim = row_limit(a.mask, a.block, my_q + shift, ks.len);  // last key this row sees
-  int n_tiles = (key_end + BN - 1) / BN;
+  int n_tiles = ks.ok ? (key_end + BN - 1) / BN : 0;
   int n_full = min(key_end, (key_full / BN) * BN) / BN;
-
   const int64_t rstride = (int64_t)a.Hkv * D;
   const T* kbase = (const T*)a.k + ks.base_row * rstride + (int64_t)g * D;
   const T* vbase = (const T*)a.v + ks.base_row * rstride + (int64_t)g * D;
@@ -460,40 +472,21 @@ __global__ void __launch_bounds__(256, 2) k_attn_flash(AttnArgs a, FlashGrid fg)
   if (n_tiles > 0) {
     dma(kbase, 0, Ks[0], koff);
     dma(vbase, 0, Vs[0], voff);
-    if (n_tiles > 1) dma(kbase, BN, Ks[1], koff);
   }
-  // Q into the operand layout (lane (l32, hi) of register c: granule 2c + hi of row l32)
-  // through this wave's quarter of Vs1, idle until the first step: 16 rows per pass, granules
-  // XOR-swizzled by row. One wavefront per region and LDS operations of a wavefront complete
-  // in order, so the passes need no barrier.
-  {
-    unsigned char* const qs = Vs1 + wave * (TILE / 4);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // the query rows and the first K/V tiles have landed
+  // Q in the operand layout: lane (l32, hi) of register c takes granule 2c + hi of row l32
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-      for (int c = pass * DC / 2; c < (pass + 1) * DC / 2; ++c) {
-        const int lr = c * RPI + lane / GPR - 16 * pass, gr = lane % GPR;
-        *(vec*)(qs + lr * ROWB + 16 * (gr ^ (lr % GPR))) = qraw[c];
-      }
-      const int lr = l32 - 16 * pass;
-      if (lr >= 0 && lr < 16) {
-#pragma unroll
-        for (int c = 0; c < DC; ++c)
-          qreg[c] = *(const vec*)(qs + lr * ROWB + 16 * ((2 * c + hi) ^ (lr % GPR)));
-      }
-    }
-  }
-  if (n_tiles > 0) {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    convert_v(Vs[0]);
-    __syncthreads();
-    qk(0, sacc[0]);
-    __syncthreads();  // every wave has read Ks[0] before tile 0's step refills it
-  }
-  // Q's loads are complete on every path from here (their values went to LDS), so the
-  // compiler counts nothing outstanding at the head of the tile loop, where a wait would
-  // also cover the next tiles' loads
+  for (int c = 0; c < DC; ++c)
+    qreg[c] = *(const vec*)(q_lds + l32 * ROWB + 16 * ((2 * c + hi) ^ sk((wave & 1) * 32 + l32)));
+  if (n_tiles > 0) convert_v(Vs[0]);
+  lds_barrier();  // every wave holds its queries (Ks1 and Vs1 are free) and V(0) is converted
+  if (n_tiles > 1) dma(kbase, BN, Ks[1], koff);
+  if (n_tiles > 0) qk(0, sacc[0]);
+  // K(1) has landed and every wave has read Ks[0] before tile 0's step refills it; nothing is
+  // outstanding at the head of the tile loop, where a wait would also cover the next tiles'
+  // loads
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
   int j = 0;
   for (; j + 2 <= n_tiles; j += 2) {
     step(j, std::integral_constant<int, 0>{});
