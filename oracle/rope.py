@@ -7,7 +7,7 @@ The streaming-cache page (flashdreams issue #763 "add an opt-in circular KV
 policy for streaming attention", section proposed boundary) states that keys
 are rotated at their absolute positions before the cache write, which is what
 lets a circular buffer hold them in physical order. It prints no RoPE formula.
-The reading taken here (every choice listed in the design notes):
+The reading taken here:
 
 * 1-D rotary embedding: coordinate pairs (a, b) of each key row are rotated by
   the angle theta = position * inv_freq[i] of their pair index i, i.e.
